@@ -1,0 +1,97 @@
+"""Packed storage of 4-bit and 3-bit signed codes, written from the bit-level definitions.
+
+The pages fix only the bit widths (W4A4, W3A3: zh §4, fr §4); the layouts
+below are this library's own and are the same for activations and weights.
+
+int4: a row of K codes (K even) becomes K/2 bytes. Byte j holds code 2j in
+      bits 0-3 and code 2j+1 in bits 4-7, each as a 4-bit two's complement.
+int3: a row of K codes (K a multiple of 32) becomes 3K/8 bytes, 12 per group
+      of 32 codes. Inside a group the 12 bytes are three 4-byte words w0, w1,
+      w2 (word k = bytes 4k..4k+3); byte lane b of a word is its byte b. Code
+      i of the group (u = its 3-bit two's complement pattern) has slot j = i//4
+      and lane b = i%4 and is stored as:
+        j = 0, 2, 4 : bits 5-7 of lane b of word j/2
+        j = 1, 3, 5 : bits 2-4 of lane b of word (j-1)/2
+        j = 6       : u bits 0-1 in bits 0-1 of lane b of w0, u bit 2 in bit 1 of lane b of w2
+        j = 7       : u bits 0-1 in bits 0-1 of lane b of w1, u bit 2 in bit 0 of lane b of w2
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def qmax(bits: int) -> int:
+    if bits not in (3, 4):
+        raise ValueError("bits must be 3 or 4")
+    return (1 << (bits - 1)) - 1
+
+
+def packed_row_bytes(k: int, bits: int) -> int:
+    if bits == 4:
+        if k % 2:
+            raise ValueError("int4 rows need an even length")
+        return k // 2
+    if bits == 3:
+        if k % 32:
+            raise ValueError("int3 rows need a multiple of 32 codes")
+        return 3 * k // 8
+    raise ValueError("bits must be 3 or 4")
+
+
+def _pattern(codes, bits):
+    c = np.asarray(codes, dtype=np.int64)
+    q = qmax(bits)
+    if np.any(c < -(q + 1)) or np.any(c > q):
+        raise ValueError("code out of range")
+    return c & ((1 << bits) - 1)
+
+
+def _signed(u, bits):
+    u = np.asarray(u, dtype=np.int64)
+    return np.where(u >= (1 << (bits - 1)), u - (1 << bits), u)
+
+
+def pack(codes, bits: int) -> np.ndarray:
+    """Pack a (rows, K) array of signed codes into (rows, packed_row_bytes(K, bits)) uint8."""
+    codes = np.atleast_2d(codes)
+    rows, k = codes.shape
+    u = _pattern(codes, bits)
+    out = np.zeros((rows, packed_row_bytes(k, bits)), dtype=np.int64)
+    if bits == 4:
+        out[:] = u[:, 0::2] | (u[:, 1::2] << 4)
+        return out.astype(np.uint8)
+    for i in range(32):
+        j, b = divmod(i, 4)
+        ui = u[:, i::32]                   # code i of every group, shape (rows, K/32)
+        cols = lambda word: 12 * np.arange(k // 32) + 4 * word + b  # noqa: E731
+        if j < 6:
+            word, shift = j // 2, (5 if j % 2 == 0 else 2)
+            out[:, cols(word)] |= ui << shift
+        else:
+            lo_word, hi_bit = (0, 1) if j == 6 else (1, 0)
+            out[:, cols(lo_word)] |= ui & 3
+            out[:, cols(2)] |= ((ui >> 2) & 1) << hi_bit
+    return out.astype(np.uint8)
+
+
+def unpack(packed, k: int, bits: int) -> np.ndarray:
+    """Inverse of ``pack``: (rows, packed bytes) uint8 -> (rows, K) int64 codes."""
+    p = np.atleast_2d(np.asarray(packed, dtype=np.int64))
+    rows = p.shape[0]
+    if p.shape[1] != packed_row_bytes(k, bits):
+        raise ValueError("packed width does not match K")
+    u = np.zeros((rows, k), dtype=np.int64)
+    if bits == 4:
+        u[:, 0::2] = p & 0xF
+        u[:, 1::2] = (p >> 4) & 0xF
+        return _signed(u, 4)
+    for i in range(32):
+        j, b = divmod(i, 4)
+        cols = lambda word: 12 * np.arange(k // 32) + 4 * word + b  # noqa: E731
+        if j < 6:
+            word, shift = j // 2, (5 if j % 2 == 0 else 2)
+            u[:, i::32] = (p[:, cols(word)] >> shift) & 7
+        else:
+            lo_word, hi_bit = (0, 1) if j == 6 else (1, 0)
+            u[:, i::32] = (p[:, cols(lo_word)] & 3) | (((p[:, cols(2)] >> hi_bit) & 1) << 2)
+    return _signed(u, 3)

@@ -1,0 +1,23 @@
+"""Seeded synthetic inputs for the ReSpinQuant online path.
+
+This package holds only random draws and the fixed workload shapes. It
+computes none of the method: no rotation, no basis-mismatch matrix, no
+subspace, no normalisation and no quantisation. Both the CPU oracle and the
+GPU path read their inputs from here, and from nothing else they share.
+"""
+from .configs import CONFIGS, Config, Linear, layer_linears
+from .generators import (
+    residual,
+    skew_generator,
+    weight,
+    linear_input,
+    outlier_channels,
+    to_bf16_bits,
+    bf16_bits_to_f32,
+)
+
+__all__ = [
+    "CONFIGS", "Config", "Linear", "layer_linears",
+    "residual", "skew_generator", "weight", "linear_input", "outlier_channels",
+    "to_bf16_bits", "bf16_bits_to_f32",
+]

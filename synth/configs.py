@@ -1,0 +1,92 @@
+"""The five synthetic workloads: shapes, value recipes and seed streams.
+
+Shapes borrow the LLaMA models the ReSpinQuant pages evaluate (technical
+summary, "Results" section: LLaMA-2 7B/13B, LLaMA-3 8B, LLaMA-3.2 1B/3B); the
+outlier channels stand in for the "extreme outliers in activation channels"
+named in each page's "Problem" section. No dataset or trained weight is used.
+
+Seed streams (``numpy.random.SeedSequence([seed_id, stream])``):
+  0 residual h, 3 outlier channel indices,
+  1/2 site-A skew generators (in/out), 13/14 site-B skew generators (in/out),
+  4..10 weights q, k, v, o, gate, up, down,
+  11 o_proj input stand-in, 12 down_proj input stand-in.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import Optional, Tuple
+
+
+@dataclass(frozen=True)
+class Config:
+    cid: int                 # workload number, 1..5
+    name: str
+    seed_id: int             # seed family (the decode workload reuses the prefill one)
+    D: int                   # hidden size (residual width)
+    F: Optional[int]         # FFN width (None: single-linear block)
+    r: int                   # headline subspace rank
+    n: int                   # tokens in the batch
+    bits: int                # weight and activation bit width (4 or 3)
+    h_dtype: str             # residual storage dtype: "bf16" or "f32"
+    y_dtype: str             # linear output dtype: "bf16" or "f32"
+    eps_rot: float           # Cayley step size of the synthetic rotations
+    n_outliers: int          # outlier channel count
+    outlier_scale: float
+    sigma_w: float           # weight standard deviation
+    kv: Optional[int] = None         # k/v projection width (GQA); None = same as D (MHA)
+    ranks: Tuple[int, ...] = ()      # ranks swept for the accuracy/throughput curve
+    decode_batches: Tuple[int, ...] = ()
+    single_linear: Optional[Tuple[int, int]] = None  # (N, K) of the one linear of a tiny block
+
+
+CONFIGS = {
+    1: Config(1, "tiny-d256-r8", 1, D=256, F=None, r=8, n=16, bits=4, h_dtype="f32",
+              y_dtype="f32", eps_rot=0.02, n_outliers=4, outlier_scale=40.0, sigma_w=0.02,
+              single_linear=(256, 256)),
+    2: Config(2, "llama2-7b-prefill-w4a4", 2, D=4096, F=11008, r=32, n=2048, bits=4,
+              h_dtype="bf16", y_dtype="bf16", eps_rot=0.01, n_outliers=20,  # 0.5% of 4096
+              outlier_scale=50.0, sigma_w=0.02, kv=None),
+    3: Config(3, "llama2-7b-decode-w4a4", 2, D=4096, F=11008, r=32, n=64, bits=4,
+              h_dtype="bf16", y_dtype="bf16", eps_rot=0.01, n_outliers=20,
+              outlier_scale=50.0, sigma_w=0.02, kv=None, decode_batches=(1, 8, 64)),
+    4: Config(4, "llama3-8b-prefill-w3a3", 4, D=4096, F=14336, r=32, n=4096, bits=3,
+              h_dtype="bf16", y_dtype="bf16", eps_rot=0.01, n_outliers=41,  # 1% of 4096
+              outlier_scale=30.0, sigma_w=0.02, kv=1024, ranks=(8, 16, 32, 64)),
+    5: Config(5, "llama2-70b-prefill-w4a4", 5, D=8192, F=28672, r=32, n=4096, bits=4,
+              h_dtype="bf16", y_dtype="bf16", eps_rot=0.01, n_outliers=25,  # 0.3% of 8192
+              outlier_scale=60.0, sigma_w=0.01, kv=1024),
+}
+
+# weight name -> seed stream
+WEIGHT_STREAMS = {"q": 4, "k": 5, "v": 6, "o": 7, "gate": 8, "up": 9, "down": 10, "proj": 4}
+SKEW_STREAMS = {("A", "in"): 1, ("A", "out"): 2, ("B", "in"): 13, ("B", "out"): 14}
+INPUT_STREAMS = {"o_in": 11, "down_in": 12}
+
+
+@dataclass(frozen=True)
+class Linear:
+    name: str                # "qkv", "o", "gate_up", "down" or "proj"
+    N: int                   # output channels
+    K: int                   # reduction width
+    source: str              # what feeds it: "siteA", "siteB", "o_in", "down_in"
+    parts: Tuple[Tuple[str, int], ...] = field(default=())  # stacked weights (name, rows)
+
+
+def layer_linears(cfg: Config, gqa: bool = True):
+    """The linears of one decoder layer in execution order.
+
+    Site A (attention input) feeds the fused q|k|v projection, the o_proj
+    input is a stand-in, site B (FFN input) feeds the fused gate|up
+    projection and the down_proj input is a stand-in.
+    """
+    if cfg.single_linear is not None:
+        N, K = cfg.single_linear
+        return [Linear("proj", N, K, "siteA", (("proj", N),))]
+    D, F = cfg.D, cfg.F
+    kv = cfg.kv if (gqa and cfg.kv is not None) else D
+    return [
+        Linear("qkv", D + 2 * kv, D, "siteA", (("q", D), ("k", kv), ("v", kv))),
+        Linear("o", D, D, "o_in", (("o", D),)),
+        Linear("gate_up", 2 * F, D, "siteB", (("gate", F), ("up", F))),
+        Linear("down", D, F, "down_in", (("down", D),)),
+    ]

@@ -1,0 +1,325 @@
+"""Pins of the oracle's online steps (CPU only).
+
+Correction: T = I identity, rank-D equals dense h T, error non-increasing in
+r, T_hat orthogonal (norm preserved), linearity, worked 2-D and embedded-plane
+cases. Norm: closed form of mean(a^2). Quantiser: brute force, symmetry,
+scale invariance, worked examples. Packing: hand-worked bytes, round trips.
+GEMM and dequantisation: brute force, closed forms and an error bound.
+"""
+import os
+
+import numpy as np
+import pytest
+
+from oracle import online, packing, prep
+from oracle.numerics import round_to_bf16
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _skew(d, seed):
+    g = np.random.default_rng(seed).standard_normal((d, d))
+    u = np.triu(g, 1)
+    return u - u.T
+
+
+def _mismatch(d, seed, eps=0.05):
+    return prep.basis_mismatch(prep.rotation(_skew(d, seed), eps), prep.rotation(_skew(d, seed + 1), eps))
+
+
+def _bf16_exact(x):
+    return round_to_bf16(x)
+
+
+# ------------------------------------------------------------ correction
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_zero_transform_is_bit_exact_identity(dtype):
+    rng = np.random.default_rng(0)
+    h = rng.standard_normal((9, 64)) * 30
+    h = _bf16_exact(h) if dtype == "bf16" else h.astype(np.float32)
+    u, _ = np.linalg.qr(rng.standard_normal((64, 8)))
+    out = online.correct(h, u.astype(np.float32), np.zeros((8, 8), np.float32), dtype)
+    assert np.array_equal(np.asarray(out, np.float64), np.asarray(h, np.float64))
+
+
+def test_global_rotation_site_is_identity():
+    # R_in = R_out: T = I, so the correction must hand back h unchanged (it §2B, nl §2B).
+    d, r = 64, 8
+    a = _skew(d, 1)
+    t = prep.basis_mismatch(prep.rotation(a, 0.02), prep.rotation(a, 0.02))
+    u, _ = prep.principal_subspace(t, r, check_gap=False)
+    m = prep.subspace_transform(t, u)
+    h = _bf16_exact(np.random.default_rng(1).standard_normal((5, d)))
+    out = online.correct(h, u.astype(np.float32), m.astype(np.float32), "bf16")
+    assert np.array_equal(out, h)
+
+
+def test_rank_d_equals_dense_product():
+    d = 64
+    t = _mismatch(d, 2, 0.1)
+    u, _ = prep.principal_subspace(t, d)
+    m = prep.subspace_transform(t, u)
+    h = np.random.default_rng(2).standard_normal((7, d))
+    exact = online.reproject(h, online.transform(online.project(h, u), m), u)
+    assert np.allclose(exact, h @ t, atol=1e-12)
+    # with float32 inputs U_r, M the float32 output stays within 1e-5 relative L2
+    out = online.correct(h, u.astype(np.float32), m.astype(np.float32), "f32").astype(np.float64)
+    assert np.linalg.norm(out - h @ t) / np.linalg.norm(h @ t) < 1e-5
+
+
+def test_error_non_increasing_in_rank():
+    d = 128
+    t = _mismatch(d, 3, 0.05)
+    h = np.random.default_rng(3).standard_normal((16, d))
+    u_all, _ = prep.principal_subspace(t, d)
+    prev = None
+    for r in (8, 16, 32, 64, d):
+        u = u_all[:, :r]
+        hp = online.reproject(h, online.transform(online.project(h, u), prep.subspace_transform(t, u)), u)
+        err = np.linalg.norm(hp - h @ t, axis=1)
+        if prev is not None:
+            assert np.all(err <= prev * (1 + 1e-9) + 1e-12)
+        prev = err
+    assert np.max(prev) < 1e-10
+
+
+def test_float32_operator_is_orthogonal_and_norm_preserving():
+    d, r = 256, 32
+    t = _mismatch(d, 4, 0.02)
+    u, _ = prep.principal_subspace(t, r)
+    m = prep.subspace_transform(t, u)
+    u32, m32 = u.astype(np.float32).astype(np.float64), m.astype(np.float32).astype(np.float64)
+    t_hat = prep.approx_operator(u32, m32)
+    assert np.max(np.abs(t_hat.T @ t_hat - np.eye(d))) < 1e-5
+    h = np.random.default_rng(4).standard_normal((32, d))
+    hp = online.reproject(h, online.transform(online.project(h, u32), m32), u32)
+    assert np.allclose(np.linalg.norm(hp, axis=1), np.linalg.norm(h, axis=1), rtol=1e-6)
+
+
+def test_linearity():
+    d, r = 64, 8
+    t = _mismatch(d, 5)
+    u, _ = prep.principal_subspace(t, r)
+    m = prep.subspace_transform(t, u)
+    rng = np.random.default_rng(5)
+    h1, h2 = rng.standard_normal((3, d)), rng.standard_normal((3, d))
+    f = lambda h: online.reproject(h, online.transform(online.project(h, u), m), u)  # noqa: E731
+    assert np.allclose(f(2.5 * h1 - 0.75 * h2), 2.5 * f(h1) - 0.75 * f(h2), atol=1e-12)
+
+
+def test_two_dimensional_rotation_worked_case():
+    theta = 0.3
+    c, s = np.cos(theta), np.sin(theta)
+    t = np.array([[c, -s], [s, c]])
+    u, sig = prep.principal_subspace(t, 2)
+    assert np.allclose(sig, [2 * np.sin(theta / 2)] * 2, atol=1e-14)
+    m = prep.subspace_transform(t, u)
+    h = np.array([[1.0, 2.0]])
+    out = online.reproject(h, online.transform(online.project(h, u), m), u)
+    assert np.allclose(out, [[1.0 * c + 2.0 * s, -1.0 * s + 2.0 * c]], atol=1e-14)
+
+
+def test_single_embedded_plane_is_captured_exactly_at_rank_two():
+    theta = 0.7
+    c, s = np.cos(theta), np.sin(theta)
+    t = np.eye(4)
+    t[1:3, 1:3] = [[c, -s], [s, c]]
+    u, sig = prep.principal_subspace(t, 2)
+    assert np.allclose(sig[2:], 0, atol=1e-14)
+    assert np.allclose(prep.approx_operator(u, prep.subspace_transform(t, u)), t, atol=1e-14)
+
+
+# ---------------------------------------------------------------- RMSNorm
+def test_rmsnorm_mean_square_closed_form():
+    rng = np.random.default_rng(6)
+    x = _bf16_exact(rng.standard_normal((10, 256)) * 3)
+    eps = 1e-5
+    a = online.rmsnorm(x, eps).astype(np.float64)
+    ms = np.mean(x * x, axis=1)
+    assert np.allclose(np.mean(a * a, axis=1), ms / (ms + eps), rtol=1e-6)
+
+
+def test_rmsnorm_scale_invariance_without_eps():
+    x = np.random.default_rng(7).standard_normal((4, 128)).astype(np.float32)
+    assert np.array_equal(online.rmsnorm(x, 0.0), online.rmsnorm(x * np.float32(8.0), 0.0))
+
+
+def test_rmsnorm_weight_multiplies_after_normalisation():
+    x = np.random.default_rng(8).standard_normal((3, 64)).astype(np.float32)
+    w = np.random.default_rng(9).standard_normal(64).astype(np.float32)
+    assert np.array_equal(online.rmsnorm(x, 1e-5, w), online.rmsnorm(x, 1e-5) * w)
+
+
+# -------------------------------------------------------------- quantiser
+def _read_table(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                rows.append([c.strip() for c in line.split("|")])
+    return rows
+
+
+def test_quantiser_worked_examples():
+    for bits, a, s, q in _read_table("quant_worked.txt"):
+        a = np.array([float(v) for v in a.split(",")], np.float32)
+        codes, scale = online.quantize(a, int(bits))
+        assert np.float32(s) == scale[0]
+        assert codes[0].tolist() == [int(v) for v in q.split(",")]
+
+
+def _brute_force_codes(a, s, qm):
+    # the nearest level q*s over all q in [-qmax, qmax]; equidistant: the even q
+    cand = np.arange(-qm, qm + 1)
+    out = []
+    for v in a:
+        dist = np.abs(np.float32(v) / np.float32(s) - cand.astype(np.float64))
+        best = np.flatnonzero(dist == dist.min())
+        out.append(int(cand[best[0]]) if len(best) == 1 else int(cand[best][cand[best] % 2 == 0][0]))
+    return out
+
+
+@pytest.mark.parametrize("bits", [3, 4])
+def test_quantiser_matches_brute_force(bits):
+    rng = np.random.default_rng(10 + bits)
+    qm = packing.qmax(bits)
+    for trial in range(200):
+        n = rng.integers(1, 9)
+        a = (rng.standard_normal(n) * 10 ** rng.uniform(-3, 3)).astype(np.float32)
+        if trial % 5 == 0:  # plant exact half-level ties
+            s0 = np.float32(0.25)
+            a = (rng.integers(-2 * qm, 2 * qm + 1, n) * s0 / 2).astype(np.float32)
+            a[0] = qm * s0
+        codes, s = online.quantize(a, bits)
+        assert codes[0].tolist() == _brute_force_codes(a, s[0], qm)
+        assert np.max(np.abs(codes)) == (qm if np.any(a != 0) else 0)
+
+
+@pytest.mark.parametrize("bits", [3, 4])
+def test_quantiser_symmetry_and_power_of_two_invariance(bits):
+    a = np.random.default_rng(20).standard_normal((6, 96)).astype(np.float32)
+    q, s = online.quantize(a, bits)
+    qn, sn = online.quantize(-a, bits)
+    assert np.array_equal(qn, -q) and np.array_equal(sn, s)
+    q2, s2 = online.quantize(a * np.float32(2.0 ** -5), bits)
+    assert np.array_equal(q2, q) and np.array_equal(s2, s * np.float32(2.0 ** -5))
+
+
+def test_quantiser_zero_row():
+    q, s = online.quantize(np.zeros((2, 64), np.float32), 4)
+    assert not q.any() and not s.any()
+
+
+# ---------------------------------------------------------------- packing
+def test_packing_hand_worked_bytes():
+    for bits, codes, expect in _read_table("packing_bytes.txt"):
+        codes = np.array([[int(v) for v in codes.split(",")]])
+        got = packing.pack(codes, int(bits))[0]
+        assert got.tolist() == [int(b, 16) for b in expect.split()], (bits, codes)
+        assert np.array_equal(packing.unpack(got[None, :], codes.shape[1], int(bits)), codes)
+
+
+@pytest.mark.parametrize("bits", [3, 4])
+def test_packing_round_trip_all_values(bits):
+    rng = np.random.default_rng(30 + bits)
+    qm = packing.qmax(bits)
+    codes = rng.integers(-qm - 1, qm + 1, size=(17, 256))
+    p = packing.pack(codes, bits)
+    assert p.shape == (17, packing.packed_row_bytes(256, bits))
+    assert np.array_equal(packing.unpack(p, 256, bits), codes)
+
+
+def test_int3_packing_single_code_positions():
+    # a single nonzero code lands in the bits its slot and lane name, nowhere else
+    for i in range(32):
+        codes = np.zeros((1, 32), np.int64)
+        codes[0, i] = -1                                    # pattern 111
+        p = packing.pack(codes, 3)[0].astype(np.int64)
+        j, b = divmod(i, 4)
+        assert bin(int(sum(int(x) << (8 * k) for k, x in enumerate(p)))).count("1") == 3
+        if j < 6:
+            assert p[4 * (j // 2) + b] == (0xE0 if j % 2 == 0 else 0x1C)
+        else:
+            assert p[4 * (j - 6) + b] == 0x03
+            assert p[8 + b] == (0x02 if j == 6 else 0x01)
+
+
+def test_packing_rejects_bad_width():
+    with pytest.raises(ValueError):
+        packing.pack(np.zeros((1, 33), np.int64), 3)
+    with pytest.raises(ValueError):
+        packing.pack(np.zeros((1, 3), np.int64), 4)
+
+
+# ------------------------------------------------------------- GEMM, dequant
+def test_gemm_matches_triple_loop():
+    rng = np.random.default_rng(40)
+    qa, qw = rng.integers(-7, 8, (5, 64)), rng.integers(-7, 8, (6, 64))
+    acc = online.gemm(qa, qw)
+    for t in range(5):
+        for j in range(6):
+            assert acc[t, j] == sum(int(qa[t, k]) * int(qw[j, k]) for k in range(64))
+
+
+def test_gemm_all_ones_weight_gives_row_sums():
+    qa = np.random.default_rng(41).integers(-7, 8, (4, 128))
+    acc = online.gemm(qa, np.ones((3, 128), np.int64))
+    assert np.array_equal(acc, np.repeat(qa.sum(axis=1)[:, None], 3, axis=1))
+
+
+def test_gemm_extreme_codes_fit_int32():
+    k = 28672
+    acc = online.gemm(np.full((1, k), -7), np.full((1, k), -7))
+    assert acc[0, 0] == 49 * k < 2 ** 31
+
+
+def test_dequant_equals_scaled_float64_sum():
+    rng = np.random.default_rng(42)
+    qa, qw = rng.integers(-7, 8, (6, 256)), rng.integers(-7, 8, (5, 256))
+    sa = rng.uniform(0.01, 1, 6).astype(np.float32)
+    sw = rng.uniform(0.001, 0.01, 5).astype(np.float32)
+    y = online.dequant(online.gemm(qa, qw), sa, sw, "f32").astype(np.float64)
+    ref = (qa * sa[:, None].astype(np.float64)) @ (qw * sw[:, None].astype(np.float64)).T
+    assert np.all(np.abs(y - ref) <= 4 * np.spacing(np.abs(y).astype(np.float32)).astype(np.float64) + 1e-30)
+
+
+def test_quantised_linear_error_bound():
+    rng = np.random.default_rng(43)
+    k = 256
+    a = rng.standard_normal((8, k)).astype(np.float32)
+    w = (rng.standard_normal((16, k)) * 0.02).astype(np.float32)
+    qa, sa = online.quantize(a, 4)
+    qw, sw = prep.quantize_weight(w, 4)
+    y = online.dequant(online.gemm(qa, qw), sa, sw, "f32").astype(np.float64)
+    exact = a.astype(np.float64) @ w.astype(np.float64).T
+    bound = (np.abs(a) @ (sw[:, None] / 2 * np.ones((1, k))).T
+             + (sa[:, None] / 2) * np.abs(w).sum(axis=1)[None, :]
+             + k * sa[:, None] * sw[None, :] / 4)
+    assert np.all(np.abs(y - exact) <= bound * (1 + 1e-6) + 1e-6 * np.abs(exact))
+
+
+def test_packed_linear_matches_unpacked():
+    rng = np.random.default_rng(44)
+    for bits in (3, 4):
+        qm = packing.qmax(bits)
+        qa, qw = rng.integers(-qm, qm + 1, (4, 64)), rng.integers(-qm, qm + 1, (8, 64))
+        sa, sw = rng.uniform(0.1, 1, 4).astype(np.float32), rng.uniform(0.1, 1, 8).astype(np.float32)
+        y, acc = online.qgemm_packed(packing.pack(qa, bits), sa, packing.pack(qw, bits), sw, 64, bits, "f32")
+        assert np.array_equal(acc, online.gemm(qa, qw))
+        assert np.array_equal(y, online.dequant(acc, sa, sw, "f32"))
+
+
+# --------------------------------------------------------------- rounding
+def test_bf16_rounding_worked_values():
+    # 1 + 2^-8 lies halfway between bf16 neighbours 1 and 1 + 2^-7: ties to even -> 1
+    assert round_to_bf16(np.array([1 + 2 ** -8]))[0] == 1.0
+    assert round_to_bf16(np.array([1 + 3 * 2 ** -8]))[0] == 1 + 2 ** -6
+    assert round_to_bf16(np.array([1 + 2 ** -8 + 2 ** -30]))[0] == 1 + 2 ** -7
+    assert round_to_bf16(np.array([-3.0]))[0] == -3.0
+    x = np.random.default_rng(45).standard_normal(1000)
+    r = round_to_bf16(x)
+    # every result has at most 8 significant bits and lies within half a bf16 ulp
+    m, e = np.frexp(r)
+    assert np.array_equal(np.ldexp(m, 8), np.rint(np.ldexp(m, 8)))
+    assert np.all(np.abs(r - x) <= np.ldexp(1.0, np.frexp(x)[1] - 9) * (1 + 1e-12))
