@@ -1,0 +1,153 @@
+/*
+ * rsq.h - C ABI of the ReSpinQuant online path on AMD Instinct MI355X (gfx950).
+ *
+ * Sources: the five gist.science summaries of "ReSpinQuant: Efficient
+ * Layer-Wise LLM Quantization via Subspace Residual Rotation Approximation"
+ * (arXiv 2604.11080), cited as <language> <section>, e.g. "zh 2.2" is the
+ * Chinese summary, technical section 2.2.
+ *
+ * Conventions (every entry point):
+ *  - Memory: the caller owns all memory. Pointers named "host" are host
+ *    pointers; every other pointer is a device pointer on the current HIP
+ *    device, at least 16-byte aligned. The library allocates nothing.
+ *  - Execution: work is enqueued on `stream` (a hipStream_t; NULL is the
+ *    null stream) and the call returns without waiting. Device faults show
+ *    at the caller's next synchronisation.
+ *  - Errors: the return value is an rsq_status. Arguments are checked before
+ *    anything is enqueued; on an error nothing is enqueued and no output is
+ *    touched. rsq_last_error() gives a message for the calling thread's last
+ *    failed call.
+ *  - Rows: a "row" is one token. Row strides (ld_*) are in elements.
+ *  - Codes: signed 4-bit codes in [-7, 7] or 3-bit codes in [-3, 3], packed
+ *    per row, K codes in rsq_packed_row_bytes(K, bits) bytes:
+ *      int4: byte j holds code 2j in bits 0-3 and code 2j+1 in bits 4-7
+ *            (two's complement nibbles);
+ *      int3: groups of 32 codes in 12 bytes = words w0, w1, w2 (4 bytes each,
+ *            byte lane b = byte b of a word); code i of a group (3-bit two's
+ *            complement u, slot j = i/4, lane b = i%4) sits at
+ *              slots 0,2,4: bits 5-7 of lane b of word j/2;
+ *              slots 1,3,5: bits 2-4 of lane b of word (j-1)/2;
+ *              slot 6: u bits 0-1 -> bits 0-1 of lane b of w0, u bit 2 -> bit 1 of lane b of w2;
+ *              slot 7: u bits 0-1 -> bits 0-1 of lane b of w1, u bit 2 -> bit 0 of lane b of w2.
+ *  - Sizes: d and k multiples of 32; n_out a multiple of 32; n >= 0 (n = 0
+ *    enqueues nothing); 1 <= r <= 64; bits 3 or 4.
+ */
+#ifndef RSQ_H
+#define RSQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    RSQ_OK = 0,
+    RSQ_ERR_INVALID_ARG = 1,   /* null pointer, negative or inconsistent size, misalignment */
+    RSQ_ERR_UNSUPPORTED = 2,   /* valid but outside what the kernels handle (e.g. r > 64) */
+    RSQ_ERR_WORKSPACE = 3,     /* workspace missing or smaller than the size query says */
+    RSQ_ERR_HIP = 4            /* the HIP runtime refused a launch or a query */
+} rsq_status;
+
+typedef enum { RSQ_F32 = 0, RSQ_BF16 = 1 } rsq_dtype;
+
+/* rsq_quant_act flags */
+#define RSQ_QA_RMSNORM 1u
+
+#define RSQ_MAX_RANK 64
+
+/* Library version (major*10000 + minor*100 + patch). */
+int rsq_version(void);
+/* Static string naming a status code. */
+const char *rsq_status_str(int status);
+/* Message of the calling thread's last failed call ("" if none). */
+const char *rsq_last_error(void);
+
+/* Bytes of one packed row of k codes (0 if k or bits is invalid). */
+size_t rsq_packed_row_bytes(int64_t k, int bits);
+
+/*
+ * Correction site (offline, once per model). The pages apply, per residual
+ * junction, y = Q^T x, then M = R_sub - I_r inside the r-dimensional
+ * subspace, then add Q (M y) back (zh 2.2 steps 1-3; fr 2C), with Q the top-r
+ * singular vectors of dT = T - I, T = R_out^T R_in (it 2C; nl 2C; fr 2C).
+ * For a row vector h this is h' = h + ((h U) M) U^T.
+ *
+ * rsq_site_prepare turns U (d x r, row-major float32) and M (r x r, row-major
+ * float32) into the device layout the kernels read: U and V = U M^T, each
+ * split into a bfloat16 high part and a bfloat16 remainder, laid out as the
+ * matrix-core operands, r padded to a multiple of 32 with zeros.
+ * site: device buffer of rsq_site_bytes(d, r) bytes, written by this call.
+ */
+size_t rsq_site_bytes(int64_t d, int r);
+rsq_status rsq_site_prepare(const float *U, const float *M, int64_t d, int r,
+                            void *site, void *stream);
+
+/*
+ * Subspace residual rotation (zh 2.2 steps 1-3; fr 2C):
+ *   h_out[t, :] = h_in[t, :] + ((h_in[t, :] U) M) U^T   for t < n,
+ * computed with float32 accumulation and rounded once (nearest-even) to
+ * h_dtype. h_in, h_out: n rows of d elements, row stride ld_h (>= d).
+ * h_in == h_out (in place) is allowed; any other overlap is not.
+ */
+rsq_status rsq_subspace_correct(const void *h_in, void *h_out, int h_dtype,
+                                int64_t n, int64_t d, int64_t ld_h,
+                                const void *site, int r, void *stream);
+
+/*
+ * Per-token symmetric activation quantisation (the A4 / A3 settings of
+ * zh 4 and fr 4), with optional RMSNorm first (flags & RSQ_QA_RMSNORM):
+ *   inv   = float32(1 / sqrt(mean_k(x^2) + eps))       (sum of squares in float64)
+ *   a     = (x * inv) * w    (float32; w = norm_w, or 1 if norm_w is NULL);
+ *           without the flag a = x
+ *   s     = max_k |a| / qmax                           (qmax = 2^(bits-1) - 1)
+ *   q     = clamp(rint(a / s), -qmax, qmax)             (float32 quotient, ties to even)
+ *   a zero row gives s = 0 and q = 0.
+ * x: n rows of k elements (x_dtype), stride ld_x. codes: n rows of
+ * rsq_packed_row_bytes(k, bits) bytes, contiguous. scales: n floats.
+ * norm_w: k floats or NULL.
+ */
+rsq_status rsq_quant_act(const void *x, int x_dtype, int64_t n, int64_t k, int64_t ld_x,
+                         unsigned flags, const float *norm_w, float eps, int bits,
+                         uint8_t *codes, float *scales, void *stream);
+
+/*
+ * Correction, RMSNorm and quantisation in one pass over the residual:
+ * rsq_subspace_correct followed by rsq_quant_act(RSQ_QA_RMSNORM) on the
+ * rounded h_out, with identical results (the norm reads h_out as stored).
+ * h_in, h_out: contiguous rows (stride d).
+ */
+rsq_status rsq_correct_quant(const void *h_in, void *h_out, int h_dtype, int64_t n, int64_t d,
+                             const void *site, int r, const float *norm_w, float eps, int bits,
+                             uint8_t *codes, float *scales, void *stream);
+
+/*
+ * Quantised linear with per-token and per-channel dequantisation (W4A4 /
+ * W3A3; a standard linear once the rotations are fused, zh 2.2 and nl 2A):
+ *   acc[t, j] = sum_k a[t, k] * w[j, k]                   (exact int32)
+ *   y[t, j]   = (float32(acc[t, j]) * a_scales[t]) * w_scales[j]   (float32), then y_dtype
+ * a_codes: n packed rows of k codes; w_codes: n_out packed rows of k codes.
+ * y: n rows, stride ld_y (>= n_out). acc_out: NULL, or n x n_out int32
+ * (contiguous) that receives the raw accumulators.
+ */
+rsq_status rsq_qgemm(const uint8_t *a_codes, const float *a_scales, int64_t n,
+                     const uint8_t *w_codes, const float *w_scales, int64_t n_out,
+                     int64_t k, int bits, void *y, int y_dtype, int64_t ld_y,
+                     int32_t *acc_out, void *stream);
+
+/*
+ * One correction site feeding its quantised linear: rsq_correct_quant then
+ * rsq_qgemm on its codes. Writes h_out, codes, scales and y (stride n_out).
+ */
+rsq_status rsq_layer_fused(const void *h_in, void *h_out, int h_dtype, int64_t n, int64_t d,
+                           const void *site, int r, const float *norm_w, float eps, int bits,
+                           uint8_t *codes, float *scales,
+                           const uint8_t *w_codes, const float *w_scales, int64_t n_out,
+                           void *y, int y_dtype, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RSQ_H */

@@ -1,0 +1,219 @@
+// C ABI: argument checks, dispatch to the kernels, error reporting.
+// Every check runs before anything is enqueued; a failed check leaves all
+// outputs untouched.
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/rsq.h"
+#include "rsq_internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+rsq_status fail(rsq_status st, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+rsq_status hip_status(hipError_t e, const char *what) {
+    if (e == hipSuccess) return RSQ_OK;
+    return fail(RSQ_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool dtype_ok(int dt) { return dt == RSQ_F32 || dt == RSQ_BF16; }
+size_t dtype_size(int dt) { return dt == RSQ_BF16 ? 2 : 4; }
+
+#define RSQ_CHECK(cond, st, ...) \
+    do {                          \
+        if (!(cond)) return fail(st, __VA_ARGS__); \
+    } while (0)
+
+rsq_status check_site(int64_t d, int r) {
+    RSQ_CHECK(d > 0 && d % 32 == 0, RSQ_ERR_INVALID_ARG, "d = %lld must be a positive multiple of 32", (long long)d);
+    RSQ_CHECK(r >= 1, RSQ_ERR_INVALID_ARG, "r = %d must be >= 1", r);
+    RSQ_CHECK(r <= RSQ_MAX_RANK, RSQ_ERR_UNSUPPORTED, "r = %d exceeds the supported maximum %d", r, RSQ_MAX_RANK);
+    RSQ_CHECK(r <= d, RSQ_ERR_INVALID_ARG, "r = %d exceeds d = %lld", r, (long long)d);
+    RSQ_CHECK(d <= (1 << 20), RSQ_ERR_UNSUPPORTED, "d = %lld too large", (long long)d);
+    int nw = 0, cpw = 0;
+    RSQ_CHECK(rsq::correct_geometry(d, &nw, &cpw), RSQ_ERR_UNSUPPORTED,
+              "d = %lld: d/32 must split into at most 8 waves of 1, 2, 4, 8, 16 or 32 chunks", (long long)d);
+    return RSQ_OK;
+}
+
+rsq_status check_bits(int bits) {
+    RSQ_CHECK(bits == 3 || bits == 4, RSQ_ERR_INVALID_ARG, "bits = %d must be 3 or 4", bits);
+    return RSQ_OK;
+}
+
+rsq_status check_correct_args(const void *h_in, const void *h_out, int h_dtype, int64_t n, int64_t d, int64_t ld_h,
+                              const void *site, int r) {
+    RSQ_CHECK(dtype_ok(h_dtype), RSQ_ERR_INVALID_ARG, "h_dtype = %d is not RSQ_F32 or RSQ_BF16", h_dtype);
+    RSQ_CHECK(n >= 0, RSQ_ERR_INVALID_ARG, "n = %lld is negative", (long long)n);
+    rsq_status st = check_site(d, r);
+    if (st != RSQ_OK) return st;
+    RSQ_CHECK(ld_h >= d, RSQ_ERR_INVALID_ARG, "ld_h = %lld < d = %lld", (long long)ld_h, (long long)d);
+    RSQ_CHECK((ld_h * (int64_t)dtype_size(h_dtype)) % 16 == 0, RSQ_ERR_INVALID_ARG,
+              "row stride of %lld bytes is not a multiple of 16", (long long)(ld_h * (int64_t)dtype_size(h_dtype)));
+    if (n == 0) return RSQ_OK;
+    RSQ_CHECK(h_in && h_out && site, RSQ_ERR_INVALID_ARG, "null pointer (h_in, h_out or site)");
+    RSQ_CHECK(aligned16(h_in) && aligned16(h_out) && aligned16(site), RSQ_ERR_INVALID_ARG,
+              "h_in, h_out and site must be 16-byte aligned");
+    if (h_in != h_out) {
+        const char *a = static_cast<const char *>(h_in), *b = static_cast<const char *>(h_out);
+        const size_t span = static_cast<size_t>((n - 1) * ld_h + d) * dtype_size(h_dtype);
+        RSQ_CHECK(a + span <= b || b + span <= a, RSQ_ERR_INVALID_ARG, "h_in and h_out overlap without being equal");
+    }
+    return RSQ_OK;
+}
+
+rsq_status check_quant_out(int64_t n, int64_t k, int bits, const uint8_t *codes, const float *scales) {
+    rsq_status st = check_bits(bits);
+    if (st != RSQ_OK) return st;
+    if (n == 0) return RSQ_OK;
+    RSQ_CHECK(codes && scales, RSQ_ERR_INVALID_ARG, "null pointer (codes or scales)");
+    RSQ_CHECK(aligned16(codes) && aligned16(scales), RSQ_ERR_INVALID_ARG, "codes and scales must be 16-byte aligned");
+    (void)k;
+    return RSQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int rsq_version(void) { return 100; }
+
+const char *rsq_status_str(int status) {
+    switch (status) {
+        case RSQ_OK: return "RSQ_OK";
+        case RSQ_ERR_INVALID_ARG: return "RSQ_ERR_INVALID_ARG";
+        case RSQ_ERR_UNSUPPORTED: return "RSQ_ERR_UNSUPPORTED";
+        case RSQ_ERR_WORKSPACE: return "RSQ_ERR_WORKSPACE";
+        case RSQ_ERR_HIP: return "RSQ_ERR_HIP";
+        default: return "RSQ_UNKNOWN_STATUS";
+    }
+}
+
+const char *rsq_last_error(void) { return g_last_error; }
+
+size_t rsq_packed_row_bytes(int64_t k, int bits) {
+    if (k <= 0 || k % 32) return 0;
+    if (bits == 4) return static_cast<size_t>(k) / 2;
+    if (bits == 3) return static_cast<size_t>(k) * 3 / 8;
+    return 0;
+}
+
+size_t rsq_site_bytes(int64_t d, int r) {
+    if (d <= 0 || d % 32 || r < 1 || r > RSQ_MAX_RANK || r > d) return 0;
+    return rsq::site_bytes(d, r);
+}
+
+rsq_status rsq_site_prepare(const float *U, const float *M, int64_t d, int r, void *site, void *stream) {
+    g_last_error[0] = 0;
+    rsq_status st = check_site(d, r);
+    if (st != RSQ_OK) return st;
+    RSQ_CHECK(U && M && site, RSQ_ERR_INVALID_ARG, "null pointer (U, M or site)");
+    RSQ_CHECK(aligned16(site), RSQ_ERR_INVALID_ARG, "site must be 16-byte aligned");
+    return hip_status(rsq::launch_site_prepare(U, M, static_cast<int>(d), r, site, static_cast<hipStream_t>(stream)),
+                      "rsq_site_prepare launch");
+}
+
+rsq_status rsq_subspace_correct(const void *h_in, void *h_out, int h_dtype, int64_t n, int64_t d, int64_t ld_h,
+                                const void *site, int r, void *stream) {
+    g_last_error[0] = 0;
+    rsq_status st = check_correct_args(h_in, h_out, h_dtype, n, d, ld_h, site, r);
+    if (st != RSQ_OK || n == 0) return st;
+    return hip_status(rsq::launch_correct(h_in, h_out, h_dtype, n, static_cast<int>(d), ld_h, site, r, false,
+                                          nullptr, 0.0f, 4, nullptr, nullptr, static_cast<hipStream_t>(stream)),
+                      "rsq_subspace_correct launch");
+}
+
+rsq_status rsq_quant_act(const void *x, int x_dtype, int64_t n, int64_t k, int64_t ld_x, unsigned flags,
+                         const float *norm_w, float eps, int bits, uint8_t *codes, float *scales, void *stream) {
+    g_last_error[0] = 0;
+    RSQ_CHECK(dtype_ok(x_dtype), RSQ_ERR_INVALID_ARG, "x_dtype = %d is not RSQ_F32 or RSQ_BF16", x_dtype);
+    RSQ_CHECK(n >= 0, RSQ_ERR_INVALID_ARG, "n = %lld is negative", (long long)n);
+    RSQ_CHECK(k > 0 && k % 32 == 0, RSQ_ERR_INVALID_ARG, "k = %lld must be a positive multiple of 32", (long long)k);
+    RSQ_CHECK(k <= 32768, RSQ_ERR_UNSUPPORTED, "k = %lld exceeds 32768", (long long)k);
+    RSQ_CHECK(ld_x >= k, RSQ_ERR_INVALID_ARG, "ld_x = %lld < k = %lld", (long long)ld_x, (long long)k);
+    RSQ_CHECK((ld_x * (int64_t)dtype_size(x_dtype)) % 16 == 0, RSQ_ERR_INVALID_ARG, "row stride not a multiple of 16 bytes");
+    RSQ_CHECK((flags & ~RSQ_QA_RMSNORM) == 0, RSQ_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+    RSQ_CHECK(!(flags & RSQ_QA_RMSNORM) || eps >= 0.0f, RSQ_ERR_INVALID_ARG, "eps must be >= 0");
+    RSQ_CHECK(n <= 0x7fffffff, RSQ_ERR_UNSUPPORTED, "n too large");
+    rsq_status st = check_quant_out(n, k, bits, codes, scales);
+    if (st != RSQ_OK || n == 0) return st;
+    RSQ_CHECK(x != nullptr && aligned16(x), RSQ_ERR_INVALID_ARG, "x must be non-null and 16-byte aligned");
+    return hip_status(rsq::launch_quant(x, x_dtype, n, static_cast<int>(k), ld_x, (flags & RSQ_QA_RMSNORM) != 0,
+                                        norm_w, eps, bits, codes, scales, static_cast<hipStream_t>(stream)),
+                      "rsq_quant_act launch");
+}
+
+rsq_status rsq_correct_quant(const void *h_in, void *h_out, int h_dtype, int64_t n, int64_t d, const void *site,
+                             int r, const float *norm_w, float eps, int bits, uint8_t *codes, float *scales,
+                             void *stream) {
+    g_last_error[0] = 0;
+    rsq_status st = check_correct_args(h_in, h_out, h_dtype, n, d, d, site, r);
+    if (st != RSQ_OK) return st;
+    RSQ_CHECK(eps >= 0.0f, RSQ_ERR_INVALID_ARG, "eps must be >= 0");
+    st = check_quant_out(n, d, bits, codes, scales);
+    if (st != RSQ_OK || n == 0) return st;
+    return hip_status(rsq::launch_correct(h_in, h_out, h_dtype, n, static_cast<int>(d), d, site, r, true, norm_w,
+                                          eps, bits, codes, scales, static_cast<hipStream_t>(stream)),
+                      "rsq_correct_quant launch");
+}
+
+rsq_status rsq_qgemm(const uint8_t *a_codes, const float *a_scales, int64_t n, const uint8_t *w_codes,
+                     const float *w_scales, int64_t n_out, int64_t k, int bits, void *y, int y_dtype, int64_t ld_y,
+                     int32_t *acc_out, void *stream) {
+    g_last_error[0] = 0;
+    rsq_status st = check_bits(bits);
+    if (st != RSQ_OK) return st;
+    RSQ_CHECK(dtype_ok(y_dtype), RSQ_ERR_INVALID_ARG, "y_dtype = %d is not RSQ_F32 or RSQ_BF16", y_dtype);
+    RSQ_CHECK(n >= 0, RSQ_ERR_INVALID_ARG, "n = %lld is negative", (long long)n);
+    RSQ_CHECK(n_out > 0 && n_out % 32 == 0, RSQ_ERR_INVALID_ARG, "n_out = %lld must be a positive multiple of 32", (long long)n_out);
+    RSQ_CHECK(k > 0 && k % 32 == 0, RSQ_ERR_INVALID_ARG, "k = %lld must be a positive multiple of 32", (long long)k);
+    RSQ_CHECK(k <= 65536, RSQ_ERR_UNSUPPORTED, "k = %lld exceeds 65536 (int32 accumulator bound)", (long long)k);
+    RSQ_CHECK(ld_y >= n_out, RSQ_ERR_INVALID_ARG, "ld_y = %lld < n_out = %lld", (long long)ld_y, (long long)n_out);
+    RSQ_CHECK(n <= 0x7fffffff && n_out <= 0x7fffffff, RSQ_ERR_UNSUPPORTED, "size too large");
+    if (n == 0) return RSQ_OK;
+    RSQ_CHECK(a_codes && a_scales && w_codes && w_scales && y, RSQ_ERR_INVALID_ARG, "null pointer");
+    RSQ_CHECK(aligned16(a_codes) && aligned16(w_codes) && aligned16(a_scales) && aligned16(w_scales) && aligned16(y),
+              RSQ_ERR_INVALID_ARG, "operands must be 16-byte aligned");
+    RSQ_CHECK(acc_out == nullptr || aligned16(acc_out), RSQ_ERR_INVALID_ARG, "acc_out must be 16-byte aligned");
+    return hip_status(rsq::launch_qgemm(a_codes, a_scales, n, w_codes, w_scales, n_out, k, bits, y, y_dtype, ld_y,
+                                        acc_out, static_cast<hipStream_t>(stream)),
+                      "rsq_qgemm launch");
+}
+
+rsq_status rsq_layer_fused(const void *h_in, void *h_out, int h_dtype, int64_t n, int64_t d, const void *site, int r,
+                           const float *norm_w, float eps, int bits, uint8_t *codes, float *scales,
+                           const uint8_t *w_codes, const float *w_scales, int64_t n_out, void *y, int y_dtype,
+                           void *stream) {
+    g_last_error[0] = 0;
+    rsq_status st = check_correct_args(h_in, h_out, h_dtype, n, d, d, site, r);
+    if (st != RSQ_OK) return st;
+    st = check_quant_out(n, d, bits, codes, scales);
+    if (st != RSQ_OK) return st;
+    RSQ_CHECK(eps >= 0.0f, RSQ_ERR_INVALID_ARG, "eps must be >= 0");
+    RSQ_CHECK(dtype_ok(y_dtype), RSQ_ERR_INVALID_ARG, "y_dtype = %d is not RSQ_F32 or RSQ_BF16", y_dtype);
+    RSQ_CHECK(n_out > 0 && n_out % 32 == 0, RSQ_ERR_INVALID_ARG, "n_out = %lld must be a positive multiple of 32", (long long)n_out);
+    RSQ_CHECK(d <= 65536, RSQ_ERR_UNSUPPORTED, "d = %lld exceeds 65536", (long long)d);
+    if (n == 0) return RSQ_OK;
+    RSQ_CHECK(w_codes && w_scales && y, RSQ_ERR_INVALID_ARG, "null pointer (w_codes, w_scales or y)");
+    RSQ_CHECK(aligned16(w_codes) && aligned16(w_scales) && aligned16(y), RSQ_ERR_INVALID_ARG, "operands must be 16-byte aligned");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    st = hip_status(rsq::launch_correct(h_in, h_out, h_dtype, n, static_cast<int>(d), d, site, r, true, norm_w, eps,
+                                        bits, codes, scales, s),
+                    "rsq_layer_fused correction launch");
+    if (st != RSQ_OK) return st;
+    return hip_status(rsq::launch_qgemm(codes, scales, n, w_codes, w_scales, n_out, d, bits, y, y_dtype, n_out,
+                                        nullptr, s),
+                      "rsq_layer_fused GEMM launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,34 @@
+// Internal launcher interface between the C ABI (rsq_api.hip) and the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace rsq {
+
+// r rounded up to a multiple of 32 (the matrix-core K step of the reprojection).
+inline int rank_pad(int r) { return (r + 31) / 32 * 32; }
+
+// Bytes of a prepared site: U and V = U M^T, each as bf16 hi + lo, d x r_pad.
+inline size_t site_bytes(int64_t d, int r) { return static_cast<size_t>(d) * rank_pad(r) * 2 * 2 * 2; }
+
+// Waves per workgroup and 32-column chunks per wave of the correction kernel
+// for width d; returns false if d cannot be split evenly.
+bool correct_geometry(int64_t d, int *waves, int *chunks_per_wave);
+
+hipError_t launch_site_prepare(const float *U, const float *M, int d, int r, void *site, hipStream_t s);
+
+// h_dtype: 0 float32, 1 bfloat16. quant: also RMSNorm + quantise + pack.
+hipError_t launch_correct(const void *h_in, void *h_out, int h_dtype, int64_t n, int d, int64_t ld_h,
+                          const void *site, int r, bool quant, const float *norm_w, float eps, int bits,
+                          uint8_t *codes, float *scales, hipStream_t s);
+
+hipError_t launch_quant(const void *x, int x_dtype, int64_t n, int k, int64_t ld_x, bool norm,
+                        const float *norm_w, float eps, int bits, uint8_t *codes, float *scales,
+                        hipStream_t s);
+
+hipError_t launch_qgemm(const uint8_t *a, const float *sa, int64_t n, const uint8_t *w, const float *sw,
+                        int64_t n_out, int64_t k, int bits, void *y, int y_dtype, int64_t ld_y,
+                        int32_t *acc_out, hipStream_t s);
+
+}  // namespace rsq

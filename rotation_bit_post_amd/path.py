@@ -1,0 +1,204 @@
+"""One decoder layer's linear path on the device, built from the C-ABI entry points.
+
+Per layer (two correction sites, one at the attention input and one at the
+FFN input, as each of the MHSA and FFN blocks carries its own rotations,
+zh 2.2):
+
+  site A: rsq_correct_quant  h -> h_A, codes, scales      (correction + RMSNorm + quant)
+          rsq_qgemm          -> y_qkv                     (fused q|k|v weights)
+          rsq_quant_act      o_proj input -> codes
+          rsq_qgemm          -> y_o
+  site B: rsq_correct_quant  h_A -> h_B, codes, scales
+          rsq_qgemm          -> y_gate_up                 (fused gate|up weights)
+          rsq_quant_act      down_proj input -> codes
+          rsq_qgemm          -> y_down
+
+The attention core, SiLU * up and the residual adds are outside this path:
+the o_proj and down_proj inputs are fixed stand-ins. With ``correction=False``
+each site runs RMSNorm + quantisation only (rsq_quant_act), the cost of a
+single global rotation (T = I), for the overhead comparison.
+
+Weights are quantised on the device with rsq_quant_act (per output channel,
+no norm); the sites come from ``offline.convert_site`` and rsq_site_prepare.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+from . import _binding as B
+from . import offline
+from synth import CONFIGS, Config, layer_linears
+from synth import generators as G
+
+
+def _dev_bf16(x: np.ndarray) -> torch.Tensor:
+    """float32 array of bf16-exact values -> bf16 device tensor (exact)."""
+    return torch.from_numpy(np.ascontiguousarray(x, np.float32)).to("cuda").to(torch.bfloat16)
+
+
+def _dev(x: np.ndarray, dtype=None) -> torch.Tensor:
+    t = torch.from_numpy(np.ascontiguousarray(x)).to("cuda")
+    return t if dtype is None else t.to(dtype)
+
+
+@dataclass
+class Site:
+    r: int
+    U: torch.Tensor
+    M: torch.Tensor
+    buf: torch.Tensor
+
+
+@dataclass
+class QLinear:
+    name: str
+    N: int
+    K: int
+    codes: torch.Tensor
+    scales: torch.Tensor
+
+
+def make_site(U: np.ndarray, M: np.ndarray) -> Site:
+    d, r = U.shape
+    buf = torch.empty(B.rsq_site_bytes(d, r), dtype=torch.uint8, device="cuda")
+    Ud, Md = _dev(U.astype(np.float32)), _dev(M.astype(np.float32))
+    B.rsq_site_prepare(Ud, Md, buf)
+    return Site(r, Ud, Md, buf)
+
+
+def quantize_weight_on_device(w: np.ndarray, bits: int, name: str = "") -> QLinear:
+    """Per-output-channel quantisation of a float32 weight with the library's kernel."""
+    N, K = w.shape
+    wd = _dev(w.astype(np.float32))
+    codes = torch.empty((N, B.rsq_packed_row_bytes(K, bits)), dtype=torch.uint8, device="cuda")
+    scales = torch.empty(N, dtype=torch.float32, device="cuda")
+    B.rsq_quant_act(wd, codes, scales, bits, rmsnorm=False)
+    del wd
+    return QLinear(name, N, K, codes, scales)
+
+
+def synthetic_site(cfg: Config, which: str, r: int):
+    """(U_r, M) of a synthetic site: rotations H C(eps A) from the seeded skew generators."""
+    a_in = G.skew_generator(cfg, which, "in")
+    a_out = G.skew_generator(cfg, which, "out")
+    r_in = offline.synthetic_rotation(a_in, cfg.eps_rot)
+    r_out = offline.synthetic_rotation(a_out, cfg.eps_rot)
+    return offline.convert_site(r_in, r_out, r)
+
+
+@dataclass
+class LayerPath:
+    cfg: Config
+    n: int
+    r: int
+    gqa: bool = True
+    eps: float = 1e-5
+    sites: dict = field(default_factory=dict)
+    linears: dict = field(default_factory=dict)
+    bufs: dict = field(default_factory=dict)
+
+    @classmethod
+    def build(cls, cid: int, n: int | None = None, r: int | None = None, gqa: bool = True,
+              sites=None, weights=None) -> "LayerPath":
+        """Device-resident inputs and outputs of one layer path.
+
+        sites: optional {"A": (U, M), "B": (U, M)}; weights: optional
+        {linear name: float32 (N, K)} - both default to the seeded synthetic ones.
+        """
+        cfg = CONFIGS[cid]
+        self = cls(cfg, n or cfg.n, r or cfg.r, gqa)
+        lins = layer_linears(cfg, gqa)
+        names = sorted({l.source for l in lins if l.source.startswith("site")})
+        for src in names:
+            which = src[-1]
+            U, M = sites[which] if sites is not None else synthetic_site(cfg, which, self.r)
+            self.sites[which] = make_site(U, M)
+        for lin in lins:
+            if weights is not None:
+                w = weights[lin.name]
+            else:
+                w = np.concatenate([G.weight(cfg, part, rows, lin.K) for part, rows in lin.parts], axis=0)
+            self.linears[lin.name] = quantize_weight_on_device(w, cfg.bits, lin.name)
+            self.linears[lin.name].source = lin.source
+            del w
+        self._alloc()
+        return self
+
+    def _alloc(self):
+        cfg, n, bits = self.cfg, self.n, self.cfg.bits
+        hdt = torch.bfloat16 if cfg.h_dtype == "bf16" else torch.float32
+        ydt = torch.bfloat16 if cfg.y_dtype == "bf16" else torch.float32
+        h = G.residual(cfg, n)
+        self.bufs["h"] = _dev_bf16(h) if hdt == torch.bfloat16 else _dev(h)
+        for which in self.sites:
+            self.bufs[f"h_{which}"] = torch.empty_like(self.bufs["h"])
+            self.bufs[f"codes_{which}"] = torch.empty((n, B.rsq_packed_row_bytes(cfg.D, bits)), dtype=torch.uint8, device="cuda")
+            self.bufs[f"scales_{which}"] = torch.empty(n, dtype=torch.float32, device="cuda")
+        for name, lin in self.linears.items():
+            self.bufs[f"y_{name}"] = torch.empty((n, lin.N), dtype=ydt, device="cuda")
+            if lin.source in ("o_in", "down_in"):
+                x = G.linear_input(cfg, lin.source, n, lin.K)
+                self.bufs[lin.source] = _dev_bf16(x) if hdt == torch.bfloat16 else _dev(x)
+                self.bufs[f"codes_{lin.source}"] = torch.empty((n, B.rsq_packed_row_bytes(lin.K, bits)), dtype=torch.uint8, device="cuda")
+                self.bufs[f"scales_{lin.source}"] = torch.empty(n, dtype=torch.float32, device="cuda")
+
+    # ------------------------------------------------------------------ run
+    def stages(self, correction: bool = True):
+        """The path as a list of (stage name, kind, callable); kind is "site", "quant" or "gemm"."""
+        cfg, bits, b = self.cfg, self.cfg.bits, self.bufs
+        out = []
+        h_cur = b["h"]
+        order = ["A", "B"] if "B" in self.sites else ["A"]
+        for which in order:
+            site = self.sites[which]
+            h_in, h_out = h_cur, b[f"h_{which}"]
+            codes, scales = b[f"codes_{which}"], b[f"scales_{which}"]
+            if correction:
+                fn = (lambda h_in=h_in, h_out=h_out, site=site, codes=codes, scales=scales:
+                      B.rsq_correct_quant(h_in, h_out, site.buf, site.r, codes, scales, bits, eps=self.eps))
+            else:
+                fn = (lambda h_in=h_in, codes=codes, scales=scales:
+                      B.rsq_quant_act(h_in, codes, scales, bits, rmsnorm=True, eps=self.eps))
+            out.append((f"site{which}", "site" if correction else "quant", fn))
+            for lin in self.linears.values():
+                if lin.source == f"site{which}":
+                    out.append(self._gemm(lin, codes, scales))
+                    break
+            h_cur = h_out if correction else h_in
+            stand_in = "o_in" if which == "A" else "down_in"
+            for lin in self.linears.values():
+                if lin.source == stand_in:
+                    x, c, s = b[stand_in], b[f"codes_{stand_in}"], b[f"scales_{stand_in}"]
+                    out.append((f"quant_{stand_in}", "quant",
+                                lambda x=x, c=c, s=s: B.rsq_quant_act(x, c, s, bits, rmsnorm=False)))
+                    out.append(self._gemm(lin, c, s))
+        return out
+
+    def _gemm(self, lin: QLinear, codes, scales):
+        y = self.bufs[f"y_{lin.name}"]
+        n, bits = self.n, self.cfg.bits
+        return (f"gemm_{lin.name}", "gemm",
+                lambda: B.rsq_qgemm(codes, scales, n, lin.codes, lin.scales, lin.N, lin.K, bits, y))
+
+    def step(self, correction: bool = True):
+        for _, _, fn in self.stages(correction):
+            fn()
+
+    # -------------------------------------------------- algorithmic work
+    def stage_work(self, name: str):
+        """(algorithmic bytes, algorithmic integer ops) of one stage launch."""
+        cfg, n, bits = self.cfg, self.n, self.cfg.bits
+        hs = 2 if cfg.h_dtype == "bf16" else 4
+        ys = 2 if cfg.y_dtype == "bf16" else 4
+        if name.startswith("site"):
+            r = self.r
+            return (n * (2 * cfg.D * hs + cfg.D * bits // 8 + 4) + 4 * cfg.D * r + 4 * r * r, 0)
+        if name.startswith("quant_"):
+            k = self.linears["o"].K if name == "quant_o_in" else self.linears["down"].K
+            return (n * (k * hs + k * bits // 8 + 4), 0)
+        lin = self.linears[name[len("gemm_"):]]
+        byts = lin.N * lin.K * bits // 8 + 4 * lin.N + n * (lin.K * bits // 8 + 4) + n * lin.N * ys
+        return (byts, 2 * n * lin.N * lin.K)

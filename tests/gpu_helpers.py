@@ -1,0 +1,82 @@
+"""Shared helpers of the GPU parity tests: device transfers and cached oracle sites."""
+from __future__ import annotations
+
+import functools
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import prep
+
+
+def require_gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("GPU test run without a visible GPU")
+
+
+def lib():
+    import rotation_bit_post_amd as rsq  # raises if librsq.so is missing: no fallback
+    return rsq
+
+
+def to_dev(x, dtype: str):
+    """numpy -> device tensor; dtype "bf16" expects bf16-exact values."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x, np.float32)).cuda()
+    return t.to(torch.bfloat16) if dtype == "bf16" else t
+
+
+def to_host(t) -> np.ndarray:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return t.float().cpu().numpy().astype(np.float64)
+    return t.cpu().numpy()
+
+
+def empty_u8(rows, cols):
+    import torch
+    return torch.empty((rows, cols), dtype=torch.uint8, device="cuda")
+
+
+def empty_f32(*shape):
+    import torch
+    return torch.empty(shape, dtype=torch.float32, device="cuda")
+
+
+@functools.lru_cache(maxsize=None)
+def oracle_site(cid: int, which: str, r: int):
+    """Oracle prep of a synthetic site (float64 SVD), cached per test session."""
+    cfg = synth.CONFIGS[cid]
+    s = prep.site(synth.skew_generator(cfg, which, "in"), synth.skew_generator(cfg, which, "out"), cfg.eps_rot, r)
+    return s["U32"], s["M32"], s["sigma"]
+
+
+@functools.lru_cache(maxsize=None)
+def oracle_basis_all(cid: int, which: str, r_max: int):
+    """U (all ranks up to r_max) and T of a site: one SVD serves a rank sweep."""
+    cfg = synth.CONFIGS[cid]
+    t = prep.basis_mismatch(prep.rotation(synth.skew_generator(cfg, which, "in"), cfg.eps_rot),
+                            prep.rotation(synth.skew_generator(cfg, which, "out"), cfg.eps_rot))
+    u, sigma = prep.principal_subspace(t, r_max)
+    return u, t, sigma
+
+
+def site_for_rank(cid: int, which: str, r: int, r_max: int = 64):
+    u, t, _ = oracle_basis_all(cid, which, r_max)
+    ur = u[:, :r]
+    m = prep.subspace_transform(t, ur)
+    return ur.astype(np.float32), m.astype(np.float32)
+
+
+def rel_l2(a, b) -> float:
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+def code_mismatch_ok(gpu_codes, ref_codes, max_frac=1e-4):
+    """Codes may differ only by one level, on at most max_frac of the elements."""
+    d = np.abs(np.asarray(gpu_codes, np.int64) - np.asarray(ref_codes, np.int64))
+    return int(d.max(initial=0)) <= 1 and float(np.mean(d != 0)) <= max_frac, int(np.sum(d != 0)), int(d.max(initial=0))

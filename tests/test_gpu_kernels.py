@@ -1,0 +1,268 @@
+"""GPU parity of each C-ABI entry point against the oracle (small and ragged shapes).
+
+Bars (taken in full from the method's stated tolerances): correction
+outputs within relative L2 1e-3 (float32 residual) or 2e-2 (bfloat16
+residual) of the float64 oracle; activation codes equal except at rounding
+ties (at most one level, on at most 1e-4 of the elements); integer
+accumulators bit-exact; dequantised outputs bit-exact when codes and scales
+are identical (both sides then do the same float32 operations).
+"""
+import numpy as np
+import pytest
+
+from oracle import online, packing, prep
+from oracle.numerics import round_to_bf16
+from gpu_helpers import (code_mismatch_ok, empty_f32, empty_u8, lib, rel_l2, require_gpu, to_dev, to_host)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def _skew(d, seed):
+    g = np.random.default_rng(seed).standard_normal((d, d))
+    u = np.triu(g, 1)
+    return u - u.T
+
+
+def random_site(d, r, seed, eps=0.05):
+    """(U32, M32) of a random mismatch T = C_out^T C_in (no Hadamard needed for any d)."""
+    t = prep.cayley(eps * _skew(d, seed + 1)).T @ prep.cayley(eps * _skew(d, seed))
+    u, _ = prep.principal_subspace(t, r)
+    return u.astype(np.float32), prep.subspace_transform(t, u).astype(np.float32)
+
+
+def residual(n, d, dtype, seed, outliers=3, scale=40.0):
+    rng = np.random.default_rng(seed)
+    h = rng.standard_normal((n, d)).astype(np.float32)
+    h[:, rng.choice(d, min(outliers, d), replace=False)] *= scale
+    return round_to_bf16(h).astype(np.float32) if dtype == "bf16" else h
+
+
+def gpu_site(U, M):
+    rsq = lib()
+    import torch
+    d, r = U.shape
+    buf = torch.empty(rsq.rsq_site_bytes(d, r), dtype=torch.uint8, device="cuda")
+    rsq.rsq_site_prepare(to_dev(U, "f32"), to_dev(M, "f32"), buf)
+    return buf
+
+
+CORRECT_CASES = [  # dtype, d, r, n
+    ("f32", 256, 8, 16), ("f32", 256, 8, 3), ("bf16", 256, 8, 17), ("bf16", 96, 8, 7),
+    ("bf16", 1024, 32, 33), ("bf16", 512, 64, 40), ("f32", 128, 16, 5), ("bf16", 2048, 2, 1),
+    ("f32", 1024, 40, 19),
+]
+
+
+@pytest.mark.parametrize("dtype,d,r,n", CORRECT_CASES)
+def test_subspace_correct_matches_oracle(dtype, d, r, n):
+    rsq = lib()
+    import torch
+    print(f"case correct dtype={dtype} d={d} r={r} n={n}", flush=True)
+    U, M = random_site(d, r, seed=d + r)
+    h = residual(n, d, dtype, seed=n)
+    site = gpu_site(U, M)
+    hd = to_dev(h, dtype)
+    out = torch.empty_like(hd)
+    rsq.rsq_subspace_correct(hd, out, site, r)
+    torch.cuda.synchronize()
+    got = to_host(out).astype(np.float64)
+    ref = np.asarray(online.correct(h, U, M, dtype), np.float64)
+    err = rel_l2(got, ref)
+    print(f"  rel_l2={err:.3e}")
+    assert err <= (1e-3 if dtype == "f32" else 2e-2)
+    if dtype == "f32":
+        assert err <= 1e-5
+    # the float32 operator is orthogonal: row norms are preserved
+    nr = np.linalg.norm(got, axis=1) / np.linalg.norm(h.astype(np.float64), axis=1)
+    assert np.max(np.abs(nr - 1)) <= (1e-5 if dtype == "f32" else 4e-3)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_zero_transform_is_identity_and_in_place_works(dtype):
+    rsq = lib()
+    import torch
+    d, r, n = 512, 32, 21
+    U, _ = random_site(d, r, seed=3)
+    h = residual(n, d, dtype, seed=4)
+    site = gpu_site(U, np.zeros((r, r), np.float32))
+    hd = to_dev(h, dtype)
+    out = torch.empty_like(hd)
+    rsq.rsq_subspace_correct(hd, out, site, r)
+    torch.cuda.synchronize()
+    assert torch.equal(out, hd)
+    # in place gives the same bits as out of place
+    U, M = random_site(d, r, seed=5)
+    site = gpu_site(U, M)
+    rsq.rsq_subspace_correct(hd, out, site, r)
+    rsq.rsq_subspace_correct(hd, hd, site, r)
+    torch.cuda.synchronize()
+    assert torch.equal(out, hd)
+
+
+def test_correct_strided_rows_and_empty_batch():
+    rsq = lib()
+    import torch
+    d, r, n = 256, 8, 9
+    U, M = random_site(d, r, seed=6)
+    site = gpu_site(U, M)
+    h = residual(n, d, "bf16", seed=7)
+    big = torch.zeros((n, d + 64), dtype=torch.bfloat16, device="cuda")
+    big[:, :d] = to_dev(h, "bf16")
+    view = big[:, :d]
+    outbig = torch.full((n, d + 64), 3.0, dtype=torch.bfloat16, device="cuda")
+    rsq.rsq_subspace_correct(view, outbig[:, :d], site, r)
+    torch.cuda.synchronize()
+    ref = online.correct(h, U, M, "bf16")
+    assert rel_l2(to_host(outbig[:, :d]), ref) < 2e-2
+    assert torch.all(outbig[:, d:] == 3.0)          # padding untouched
+    empty = torch.empty((0, d), dtype=torch.bfloat16, device="cuda")
+    rsq.rsq_subspace_correct(empty, empty, site, r)  # n = 0 enqueues nothing
+
+
+QUANT_CASES = [  # dtype, n, k, bits, norm, weighted
+    ("bf16", 7, 4096, 4, True, False), ("bf16", 64, 4096, 3, True, False), ("f32", 16, 256, 4, True, False),
+    ("bf16", 5, 11008, 4, False, False), ("bf16", 3, 14336, 3, False, False), ("f32", 9, 96, 3, True, True),
+    ("bf16", 33, 1024, 4, True, True), ("bf16", 2, 28672, 4, False, False), ("f32", 130, 32, 4, False, False),
+]
+
+
+@pytest.mark.parametrize("dtype,n,k,bits,norm,weighted", QUANT_CASES)
+def test_quant_act_matches_oracle(dtype, n, k, bits, norm, weighted):
+    rsq = lib()
+    import torch
+    print(f"case quant dtype={dtype} n={n} k={k} bits={bits} norm={norm} w={weighted}", flush=True)
+    x = residual(n, k, dtype, seed=k + n, outliers=5, scale=30.0)
+    if n > 2:
+        x[1] = 0.0                                   # an all-zero row
+    w = np.random.default_rng(1).uniform(0.5, 1.5, k).astype(np.float32) if weighted else None
+    codes = empty_u8(n, rsq.rsq_packed_row_bytes(k, bits))
+    scales = empty_f32(n)
+    rsq.rsq_quant_act(to_dev(x, dtype), codes, scales, bits, rmsnorm=norm,
+                      norm_w=None if w is None else to_dev(w, "f32"), eps=1e-5)
+    torch.cuda.synchronize()
+    q_ref, s_ref = online.quant_act(x, bits, norm, 1e-5, w)
+    q_gpu = packing.unpack(codes.cpu().numpy(), k, bits)
+    s_gpu = scales.cpu().numpy()
+    ok, nbad, dmax = code_mismatch_ok(q_gpu, q_ref)
+    print(f"  code mismatches={nbad} max_level_diff={dmax}; scale max rel={np.max(np.abs(s_gpu - s_ref) / np.maximum(s_ref, 1e-30)):.2e}")
+    assert ok
+    assert np.all(np.abs(s_gpu - s_ref) <= 1e-6 * np.abs(s_ref))
+    if n > 2:
+        assert s_gpu[1] == 0 and not q_gpu[1].any()
+
+
+def test_fused_correct_quant_equals_unfused_and_oracle():
+    rsq = lib()
+    import torch
+    for dtype, d, r, n, bits in [("bf16", 1024, 32, 45, 4), ("bf16", 512, 16, 8, 3), ("f32", 256, 8, 16, 4)]:
+        print(f"case fused dtype={dtype} d={d} r={r} n={n} bits={bits}", flush=True)
+        U, M = random_site(d, r, seed=11)
+        site = gpu_site(U, M)
+        h = residual(n, d, dtype, seed=12)
+        hd = to_dev(h, dtype)
+        rb = rsq.rsq_packed_row_bytes(d, bits)
+        h1, c1, s1 = torch.empty_like(hd), empty_u8(n, rb), empty_f32(n)
+        rsq.rsq_correct_quant(hd, h1, site, r, c1, s1, bits)
+        h2, c2, s2 = torch.empty_like(hd), empty_u8(n, rb), empty_f32(n)
+        rsq.rsq_subspace_correct(hd, h2, site, r)
+        rsq.rsq_quant_act(h2, c2, s2, bits, rmsnorm=True)
+        torch.cuda.synchronize()
+        assert torch.equal(h1, h2) and torch.equal(c1, c2) and torch.equal(s1, s2)
+        # against the oracle: h' within tolerance, codes from the oracle quantiser on the GPU's h'
+        assert rel_l2(to_host(h1), online.correct(h, U, M, dtype)) <= (1e-3 if dtype == "f32" else 2e-2)
+        q_ref, s_ref = online.quant_act(to_host(h1), bits, True, 1e-5)
+        ok, nbad, _ = code_mismatch_ok(packing.unpack(c1.cpu().numpy(), d, bits), q_ref)
+        assert ok, nbad
+        assert np.all(np.abs(s1.cpu().numpy() - s_ref) <= 1e-6 * s_ref)
+
+
+GEMM_CASES = [  # bits, n, N, K, y dtype
+    (4, 1, 32, 32, "f32"), (4, 5, 96, 96, "bf16"), (3, 7, 64, 224, "f32"), (4, 64, 256, 256, "bf16"),
+    (3, 65, 288, 4096, "bf16"), (4, 130, 256, 4096, "f32"), (4, 33, 512, 11008, "bf16"), (3, 200, 160, 1056, "f32"),
+    (4, 300, 4096, 512, "bf16"),
+]
+
+
+def _random_codes(rows, k, bits, rng, extremes=True):
+    qm = packing.qmax(bits)
+    q = rng.integers(-qm, qm + 1, (rows, k))
+    if extremes and rows > 0:
+        q[0, : min(k, 64)] = -qm
+    return q
+
+
+@pytest.mark.parametrize("bits,n,N,K,ydt", GEMM_CASES)
+def test_qgemm_bit_exact(bits, n, N, K, ydt):
+    rsq = lib()
+    import torch
+    print(f"case qgemm bits={bits} n={n} N={N} K={K} y={ydt}", flush=True)
+    rng = np.random.default_rng(n * 7 + N + K)
+    qa, qw = _random_codes(n, K, bits, rng), _random_codes(N, K, bits, rng)
+    sa = rng.uniform(0.01, 2.0, n).astype(np.float32)
+    sw = rng.uniform(1e-3, 1e-2, N).astype(np.float32)
+    a_dev = torch.from_numpy(packing.pack(qa, bits)).cuda()
+    w_dev = torch.from_numpy(packing.pack(qw, bits)).cuda()
+    y = torch.empty((n, N), dtype=torch.bfloat16 if ydt == "bf16" else torch.float32, device="cuda")
+    acc = torch.empty((n, N), dtype=torch.int32, device="cuda")
+    rsq.rsq_qgemm(a_dev, to_dev(sa, "f32"), n, w_dev, to_dev(sw, "f32"), N, K, bits, y, acc_out=acc)
+    torch.cuda.synchronize()
+    acc_ref = online.gemm(qa, qw)
+    assert np.array_equal(acc.cpu().numpy().astype(np.int64), acc_ref)
+    y_ref = online.dequant(acc_ref, sa, sw, ydt)
+    assert np.array_equal(to_host(y).astype(np.float64), np.asarray(y_ref, np.float64))
+    # a second run gives the same bits (no order-dependent reductions)
+    y2 = torch.empty_like(y)
+    rsq.rsq_qgemm(a_dev, to_dev(sa, "f32"), n, w_dev, to_dev(sw, "f32"), N, K, bits, y2)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2)
+
+
+def test_qgemm_strided_output_and_minimum_codes():
+    rsq = lib()
+    import torch
+    n, N, K, bits = 40, 96, 128, 4
+    # -8 is outside the quantiser's range but inside the int4 format: the kernel must still be exact
+    qa = np.full((n, K), -8)
+    qw = np.full((N, K), -8)
+    sa = np.ones(n, np.float32)
+    sw = np.ones(N, np.float32)
+    y = torch.full((n, N + 32), -1.0, dtype=torch.float32, device="cuda")
+    acc = torch.empty((n, N), dtype=torch.int32, device="cuda")
+    rsq.rsq_qgemm(torch.from_numpy(packing.pack(qa, bits)).cuda(), to_dev(sa, "f32"), n,
+                  torch.from_numpy(packing.pack(qw, bits)).cuda(), to_dev(sw, "f32"), N, K, bits, y[:, :N], acc_out=acc)
+    torch.cuda.synchronize()
+    assert torch.all(acc == 64 * K)
+    assert torch.all(y[:, :N] == float(64 * K)) and torch.all(y[:, N:] == -1.0)
+
+
+def test_layer_fused_matches_oracle():
+    rsq = lib()
+    import torch
+    d, r, n, N, bits = 256, 8, 16, 256, 4
+    U, M = random_site(d, r, seed=21)
+    site = gpu_site(U, M)
+    h = residual(n, d, "f32", seed=22)
+    w = (np.random.default_rng(23).standard_normal((N, d)) * 0.02).astype(np.float32)
+    qw, sw = prep.quantize_weight(w, bits)
+    wp = packing.pack(qw, bits)
+    hd = to_dev(h, "f32")
+    h_out, codes, scales = torch.empty_like(hd), empty_u8(n, d // 2), empty_f32(n)
+    y = torch.empty((n, N), dtype=torch.float32, device="cuda")
+    rsq.rsq_layer_fused(hd, h_out, site, r, codes, scales, torch.from_numpy(wp).cuda(), to_dev(sw, "f32"), N, y, bits)
+    torch.cuda.synchronize()
+    ref = online.layer_fused(h, U, M, "f32", bits, 1e-5, wp, sw, "f32")
+    assert rel_l2(to_host(h_out), ref["h_out"]) < 1e-5
+    # downstream stages on the GPU's own h': codes, scales and y must then agree exactly
+    q_ref, s_ref = online.quant_act(to_host(h_out), bits, True, 1e-5)
+    q_gpu = packing.unpack(codes.cpu().numpy(), d, bits)
+    assert code_mismatch_ok(q_gpu, q_ref)[0]
+    s_gpu = scales.cpu().numpy()
+    assert np.all(np.abs(s_gpu - s_ref) <= 1e-6 * s_ref)
+    y_ref = online.dequant(online.gemm(q_gpu, qw), s_gpu, sw, "f32")
+    assert np.array_equal(to_host(y), y_ref)
+    assert rel_l2(to_host(y), ref["y"]) < 1e-2
