@@ -1,0 +1,216 @@
+"""Throughput of one decoder layer's linear path (ReSpinQuant online path) on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--config 2] [--copies 2] [--no-cpu-baseline]
+
+A step is one pass of the whole path over one batch: two correction sites
+(correction + RMSNorm + per-token quantisation), two stand-in activation
+quantisations (o_proj and down_proj inputs) and the four quantised linears
+(q|k|v, o, gate|up, down). Inputs are resident in HBM before timing starts.
+``--copies`` independent copies of every buffer are cycled so that a step
+does not find the previous step's data in the 256 MB Infinity Cache.
+
+Prints one JSON line. ``roofline`` describes the dominant kernel (the
+quantised GEMM); ``stages`` gives every stage's time and roofline fraction;
+``cpu_baseline`` is the CPU oracle timed on a bounded sample of the same
+workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 matrix-core peak
+METRIC = "tokens/s per decoder-layer linear path (W4A4, D=4096, r=32); % HBM / MFMA peak"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--config", type=int, default=2)
+    p.add_argument("--copies", type=int, default=2)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-sample", type=int, default=16, help="tokens in the CPU oracle sample")
+    return p.parse_args()
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "rotation_bit_post_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(cid: int, src_hash: str):
+    """HBM bytes per GEMM launch from the committed rocprofv3 counter summary, if it is current."""
+    path = os.path.join(ROOT, "profiles", f"qgemm_traffic_config{cid}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_hash") != src_hash:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(path, n_sample: int):
+    """The CPU oracle (unchanged) on the first n_sample tokens of the same workload."""
+    import numpy as np
+    from oracle import online
+    from synth import generators as G
+    import threadpoolctl
+
+    cfg, bits = path.cfg, path.cfg.bits
+    h = G.residual(cfg, n_sample)
+    sites = {w: (s.U.cpu().numpy(), s.M.cpu().numpy()) for w, s in path.sites.items()}
+    weights = {name: (lin.codes.cpu().numpy(), lin.scales.cpu().numpy()) for name, lin in path.linears.items()}
+    o_in = G.linear_input(cfg, "o_in", n_sample, cfg.D)
+    down_in = G.linear_input(cfg, "down_in", n_sample, cfg.F)
+    with threadpoolctl.threadpool_limits(limits=os.cpu_count()):
+        info = threadpoolctl.threadpool_info()
+        threads = max([i.get("num_threads", 1) for i in info] or [1])
+        t0 = time.perf_counter()
+        online.layer_linear_path(h, sites["A"], sites["B"], weights, o_in, down_in, cfg.h_dtype, bits,
+                                 path.eps, cfg.y_dtype)
+        dt = time.perf_counter() - t0
+    return {"value": n_sample / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {n_sample} tokens of the same workload, whole layer linear path "
+                      f"(2 corrections + norms + quantisation + 4 GEMMs with the oracle's packed-code unpacking), "
+                      f"float64 numpy; {dt:.1f} s wall"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build measures one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+    from rotation_bit_post_amd.path import LayerPath
+
+    torch.cuda.set_device(0)
+    t_build = time.perf_counter()
+    base = LayerPath.build(args.config)
+    copies = [base] + [base.clone() for _ in range(args.copies - 1)]
+    torch.cuda.synchronize()
+    t_build = time.perf_counter() - t_build
+    cfg, n = base.cfg, base.n
+    stage_lists = [p.stages(correction=True) for p in copies]
+    names = [s[0] for s in stage_lists[0]]
+    kinds = {s[0]: s[1] for s in stage_lists[0]}
+
+    for i in range(args.warmup):
+        for _, _, fn in stage_lists[i % len(copies)]:
+            fn()
+    torch.cuda.synchronize()
+
+    # timed region: events between stages on the stream the library launches on
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        stages = stage_lists[i % len(copies)]
+        ev[i][0].record(stream)
+        for j, (_, _, fn) in enumerate(stages):
+            fn()
+            ev[i][j + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_ms = [ev[i][0].elapsed_time(ev[i][-1]) for i in range(args.steps)]
+    stage_ms = {nm: [ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(args.steps)] for j, nm in enumerate(names)}
+    ms_per_step = sum(step_ms) / len(step_ms)
+
+    # correction off: each site only normalises and quantises (one global rotation, T = I)
+    off_lists = [p.stages(correction=False) for p in copies]
+    for i in range(args.warmup):
+        for _, _, fn in off_lists[i % len(copies)]:
+            fn()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(args.steps):
+        for _, _, fn in off_lists[i % len(copies)]:
+            fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_off = e0.elapsed_time(e1) / args.steps
+
+    stages_out = {}
+    gemm_ops = gemm_ms = gemm_launches = 0
+    for nm in names:
+        byts, ops = base.stage_work(nm)
+        t = sum(stage_ms[nm]) / args.steps
+        rec = {"kind": kinds[nm], "ms": round(t, 5), "alg_bytes": byts}
+        rec["hbm_frac"] = round(byts / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+        if ops:
+            rec["alg_ops"] = ops
+            rec["mfma_frac"] = round(ops / (t * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4)
+            gemm_ops += ops
+            gemm_ms += t
+            gemm_launches += 1
+        stages_out[nm] = rec
+
+    src_hash = kernel_source_hash()
+    achieved = gemm_ops / (gemm_ms * 1e-3) / 1e12
+    traffic = measured_traffic(args.config, src_hash)
+    value = n / (ms_per_step * 1e-3)
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic (seeded N(0,1) residual with outlier channels, Hadamard*Cayley rotations, N(0,sigma) weights; no dataset, no trained weights)",
+        "config": {
+            "workload": f"{cfg.name}: D={cfg.D}, FFN={cfg.F}, r={base.r}, {n} tokens, {cfg.h_dtype} residual, "
+                        f"W{cfg.bits}A{cfg.bits}; one layer's linear path = 2 correction sites + 2 stand-in "
+                        f"quantisations + GEMMs qkv {base.linears['qkv'].N}x{cfg.D}, o {cfg.D}x{cfg.D}, "
+                        f"gate|up {base.linears['gate_up'].N}x{cfg.D}, down {cfg.D}x{cfg.F}",
+            "tokens": n, "D": cfg.D, "ffn": cfg.F, "r": base.r, "bits": cfg.bits, "buffer_copies": len(copies),
+        },
+        "roofline": {
+            "kernel": "qgemm_kernel (int4 codes on v_mfma_i32_32x32x32_i8), all 4 launches of a step",
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": INT8_PEAK_TOPS,
+            "unit": "TOP/s",
+            "frac": round(achieved / INT8_PEAK_TOPS, 4),
+            "traffic": traffic,
+            "avg_launch_ms": round(gemm_ms / max(gemm_launches, 1), 5),
+        },
+        "stages": stages_out,
+        "correction_overhead": {
+            "ms_per_step_correction_off": round(ms_off, 5),
+            "overhead_frac": round(ms_per_step / ms_off - 1.0, 4),
+            "note": "same path with each site reduced to RMSNorm + quantisation (T = I, a single global rotation)",
+        },
+        "wall_s_timed": round(wall, 3),
+        "setup_s": round(t_build, 1),
+        "kernel_source_hash": src_hash,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(base, args.cpu_sample)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

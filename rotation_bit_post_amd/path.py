@@ -59,6 +59,7 @@ class QLinear:
     K: int
     codes: torch.Tensor
     scales: torch.Tensor
+    source: str = ""
 
 
 def make_site(U: np.ndarray, M: np.ndarray) -> Site:
@@ -121,11 +122,21 @@ class LayerPath:
                 w = weights[lin.name]
             else:
                 w = np.concatenate([G.weight(cfg, part, rows, lin.K) for part, rows in lin.parts], axis=0)
-            self.linears[lin.name] = quantize_weight_on_device(w, cfg.bits, lin.name)
-            self.linears[lin.name].source = lin.source
+            q = quantize_weight_on_device(w, cfg.bits, lin.name)
+            q.source = lin.source
+            self.linears[lin.name] = q
             del w
         self._alloc()
         return self
+
+    def clone(self) -> "LayerPath":
+        """An independent copy of every device buffer (same values)."""
+        other = LayerPath(self.cfg, self.n, self.r, self.gqa, self.eps)
+        other.sites = {k: Site(v.r, v.U.clone(), v.M.clone(), v.buf.clone()) for k, v in self.sites.items()}
+        other.linears = {k: QLinear(v.name, v.N, v.K, v.codes.clone(), v.scales.clone(), v.source)
+                         for k, v in self.linears.items()}
+        other.bufs = {k: v.clone() for k, v in self.bufs.items()}
+        return other
 
     def _alloc(self):
         cfg, n, bits = self.cfg, self.n, self.cfg.bits

@@ -1,0 +1,224 @@
+"""GPU parity at the five workloads' real sizes, in the launch configurations the benchmark uses.
+
+Small outputs are compared in full; GEMM outputs at full size are compared on
+sampled (token, channel) blocks that the oracle computes directly. Sites come
+from the oracle's float64 prep (SVD of T - I), weights from the seeded draws.
+"""
+import numpy as np
+import pytest
+
+import synth
+from oracle import online, packing, prep
+from gpu_helpers import (code_mismatch_ok, empty_f32, empty_u8, lib, oracle_basis_all, oracle_site, rel_l2,
+                         require_gpu, site_for_rank, to_dev, to_host)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def gpu_site(U, M):
+    import torch
+    rsq = lib()
+    d, r = U.shape
+    buf = torch.empty(rsq.rsq_site_bytes(d, r), dtype=torch.uint8, device="cuda")
+    rsq.rsq_site_prepare(to_dev(U, "f32"), to_dev(M, "f32"), buf)
+    return buf
+
+
+def run_site(h_dev, U, M, bits, dtype):
+    """GPU correction + norm + quant of one site; returns (h' device, codes, scales)."""
+    import torch
+    rsq = lib()
+    n, d = h_dev.shape
+    out = torch.empty_like(h_dev)
+    codes, scales = empty_u8(n, rsq.rsq_packed_row_bytes(d, bits)), empty_f32(n)
+    rsq.rsq_correct_quant(h_dev, out, gpu_site(U, M), U.shape[1], codes, scales, bits)
+    torch.cuda.synchronize()
+    return out, codes, scales
+
+
+def check_site(h, U, M, dtype, bits, out, codes, scales):
+    """Correction within the stated bar; codes/scales against the oracle quantiser on the GPU's h'."""
+    d = h.shape[1]
+    hp = to_host(out)
+    ref = online.correct(h, U, M, dtype)
+    err = rel_l2(hp, ref)
+    norm_dev = np.max(np.abs(np.linalg.norm(hp, axis=1) / np.linalg.norm(np.asarray(h, np.float64), axis=1) - 1))
+    q_ref, s_ref = online.quant_act(hp, bits, True, 1e-5)
+    q_gpu = packing.unpack(codes.cpu().numpy(), d, bits)
+    ok, nbad, dmax = code_mismatch_ok(q_gpu, q_ref)
+    s_gpu = scales.cpu().numpy()
+    srel = float(np.max(np.abs(s_gpu - s_ref) / s_ref))
+    print(f"  correction rel_l2={err:.3e} norm_dev={norm_dev:.2e} tie_codes={nbad} scale_max_rel={srel:.1e}", flush=True)
+    assert err <= (1e-3 if dtype == "f32" else 2e-2)
+    assert norm_dev <= (1e-5 if dtype == "f32" else 4e-3)
+    assert ok
+    assert srel <= 1e-6
+    return hp, q_gpu, s_gpu
+
+
+def gemm_sampled(bits, n, N, K, seed, rows=None, cols=None, y_dtype="bf16"):
+    """Full-size GEMM on the GPU from random codes; the oracle checks sampled rows x columns."""
+    import torch
+    rsq = lib()
+    rng = np.random.default_rng(seed)
+    rb = packing.packed_row_bytes(K, bits)
+    if bits == 4:
+        a_bytes = rng.integers(0, 256, (n, rb), dtype=np.uint8)
+        w_bytes = rng.integers(0, 256, (N, rb), dtype=np.uint8)
+    else:
+        qm = packing.qmax(bits)
+        a_bytes = packing.pack(rng.integers(-qm, qm + 1, (n, K)), bits)
+        w_bytes = packing.pack(rng.integers(-qm, qm + 1, (N, K)), bits)
+    sa = rng.uniform(0.01, 1.0, n).astype(np.float32)
+    sw = rng.uniform(1e-3, 1e-2, N).astype(np.float32)
+    y = torch.empty((n, N), dtype=torch.bfloat16 if y_dtype == "bf16" else torch.float32, device="cuda")
+    acc = torch.empty((n, N), dtype=torch.int32, device="cuda")
+    rsq.rsq_qgemm(torch.from_numpy(a_bytes).cuda(), to_dev(sa, "f32"), n, torch.from_numpy(w_bytes).cuda(),
+                  to_dev(sw, "f32"), N, K, bits, y, acc_out=acc)
+    torch.cuda.synchronize()
+    rows = rows if rows is not None else np.unique(np.r_[0, rng.choice(n, min(n, 96), replace=False), n - 1])
+    cols = cols if cols is not None else np.unique(np.r_[0, rng.choice(N, min(N, 384), replace=False), N - 1])
+    qa = packing.unpack(a_bytes[rows], K, bits)
+    qw = packing.unpack(w_bytes[cols], K, bits)
+    acc_ref = online.gemm(qa, qw)
+    acc_gpu = acc[torch.from_numpy(rows).cuda()][:, torch.from_numpy(cols).cuda()].cpu().numpy().astype(np.int64)
+    assert np.array_equal(acc_gpu, acc_ref)
+    y_ref = online.dequant(acc_ref, sa[rows], sw[cols], y_dtype)
+    y_gpu = to_host(y[torch.from_numpy(rows).cuda()][:, torch.from_numpy(cols).cuda()])
+    assert np.array_equal(np.asarray(y_gpu, np.float64), np.asarray(y_ref, np.float64))
+    print(f"  gemm bits={bits} n={n} N={N} K={K}: {len(rows)}x{len(cols)} sampled outputs bit-exact", flush=True)
+
+
+# ------------------------------------------------------------------ config 1
+def test_config1_tiny_block_end_to_end():
+    import torch
+    rsq = lib()
+    cfg = synth.CONFIGS[1]
+    U, M, _ = oracle_site(1, "A", cfg.r)
+    h = synth.residual(cfg)
+    w = synth.weight(cfg, "proj", *cfg.single_linear)
+    qw, sw = prep.quantize_weight(w, cfg.bits)
+    wp = packing.pack(qw, cfg.bits)
+    N = cfg.single_linear[0]
+    hd = to_dev(h, "f32")
+    h_out, codes, scales = torch.empty_like(hd), empty_u8(cfg.n, cfg.D // 2), empty_f32(cfg.n)
+    y = torch.empty((cfg.n, N), dtype=torch.float32, device="cuda")
+    rsq.rsq_layer_fused(hd, h_out, gpu_site(U, M), cfg.r, codes, scales, torch.from_numpy(wp).cuda(),
+                        to_dev(sw, "f32"), N, y, cfg.bits)
+    torch.cuda.synchronize()
+    hp, q_gpu, s_gpu = check_site(h, U, M, "f32", cfg.bits, h_out, codes, scales)
+    ref = online.layer_fused(h, U, M, "f32", cfg.bits, 1e-5, wp, sw, "f32")
+    assert np.array_equal(to_host(y), online.dequant(online.gemm(q_gpu, qw), s_gpu, sw, "f32"))
+    if np.array_equal(q_gpu, ref["q"]):
+        assert rel_l2(to_host(y), ref["y"]) < 1e-6
+    # the device weight quantiser reproduces the oracle's weight codes
+    wc, ws = empty_u8(N, cfg.D // 2), empty_f32(N)
+    rsq.rsq_quant_act(to_dev(w, "f32"), wc, ws, cfg.bits)
+    torch.cuda.synchronize()
+    assert code_mismatch_ok(packing.unpack(wc.cpu().numpy(), cfg.D, cfg.bits), qw)[0]
+    assert np.all(np.abs(ws.cpu().numpy() - sw) <= 1e-6 * sw)
+
+
+# ------------------------------------------------------------- configs 2, 3
+def test_config2_both_sites_full_batch():
+    cfg = synth.CONFIGS[2]
+    h = synth.residual(cfg)
+    print(f"case config2 sites n={cfg.n} d={cfg.D} r={cfg.r}", flush=True)
+    UA, MA, _ = oracle_site(2, "A", cfg.r)
+    outA, cA, sA = run_site(to_dev(h, "bf16"), UA, MA, cfg.bits, "bf16")
+    hA, _, _ = check_site(h, UA, MA, "bf16", cfg.bits, outA, cA, sA)
+    UB, MB, _ = oracle_site(2, "B", cfg.r)
+    outB, cB, sB = run_site(outA, UB, MB, cfg.bits, "bf16")
+    check_site(hA, UB, MB, "bf16", cfg.bits, outB, cB, sB)
+
+
+@pytest.mark.parametrize("name,N,K", [("qkv", 12288, 4096), ("o", 4096, 4096), ("gate_up", 22016, 4096),
+                                      ("down", 4096, 11008)])
+def test_config2_gemms_full_size(name, N, K):
+    print(f"case config2 gemm {name}", flush=True)
+    gemm_sampled(4, 2048, N, K, seed=N + K)
+
+
+def test_config2_weight_quantisation_on_device():
+    import torch
+    rsq = lib()
+    cfg = synth.CONFIGS[2]
+    w = np.concatenate([synth.weight(cfg, p, cfg.D, cfg.D) for p in ("q", "k", "v")], axis=0)
+    wc, ws = empty_u8(w.shape[0], cfg.D // 2), empty_f32(w.shape[0])
+    rsq.rsq_quant_act(to_dev(w, "f32"), wc, ws, cfg.bits)
+    torch.cuda.synchronize()
+    qw, sw = prep.quantize_weight(w, cfg.bits)
+    ok, nbad, _ = code_mismatch_ok(packing.unpack(wc.cpu().numpy(), cfg.D, cfg.bits), qw)
+    assert ok, nbad
+    assert np.all(np.abs(ws.cpu().numpy() - sw) <= 1e-6 * sw)
+
+
+@pytest.mark.parametrize("n", [1, 8, 64])
+def test_config3_decode_batches(n):
+    import torch
+    rsq = lib()
+    cfg = synth.CONFIGS[3]
+    print(f"case config3 decode n={n}", flush=True)
+    h = synth.residual(cfg, n)
+    assert np.array_equal(h, synth.residual(synth.CONFIGS[2], 2048)[:n])   # head of the prefill batch
+    UA, MA, _ = oracle_site(2, "A", cfg.r)
+    out, codes, scales = run_site(to_dev(h, "bf16"), UA, MA, cfg.bits, "bf16")
+    _, q_gpu, s_gpu = check_site(h, UA, MA, "bf16", cfg.bits, out, codes, scales)
+    # q|k|v projection with the real quantised weights, every output checked
+    w = np.concatenate([synth.weight(cfg, p, cfg.D, cfg.D) for p in ("q", "k", "v")], axis=0)
+    qw, sw = prep.quantize_weight(w, cfg.bits)
+    wp = packing.pack(qw, cfg.bits)
+    y = torch.empty((n, w.shape[0]), dtype=torch.bfloat16, device="cuda")
+    rsq.rsq_qgemm(codes, scales, n, torch.from_numpy(wp).cuda(), to_dev(sw, "f32"), w.shape[0], cfg.D, cfg.bits, y)
+    torch.cuda.synchronize()
+    y_ref = online.dequant(online.gemm(q_gpu, qw), s_gpu, sw, "bf16")
+    assert np.array_equal(to_host(y), y_ref)
+    for N, K in [(4096, 4096), (22016, 4096), (4096, 11008)]:
+        gemm_sampled(4, n, N, K, seed=n + N, rows=np.arange(n))
+
+
+# ------------------------------------------------------------------ config 4
+def test_config4_w3a3_rank_sweep():
+    cfg = synth.CONFIGS[4]
+    h = synth.residual(cfg)
+    hd = to_dev(h, "bf16")
+    _, T, _ = oracle_basis_all(4, "A", 64)
+    dense = np.asarray(h, np.float64) @ T
+    errs = []
+    for r in cfg.ranks:
+        print(f"case config4 site r={r}", flush=True)
+        U, M = site_for_rank(4, "A", r)
+        out, codes, scales = run_site(hd, U, M, 3, "bf16")
+        hp, _, _ = check_site(h, U, M, "bf16", 3, out, codes, scales)
+        errs.append(rel_l2(hp, dense))
+    print(f"  approximation error vs dense h T by rank {dict(zip(cfg.ranks, [round(e, 4) for e in errs]))}")
+    # more rank never increases the approximation error (beyond bf16 output rounding)
+    assert all(b <= a + 2e-3 for a, b in zip(errs, errs[1:]))
+
+
+@pytest.mark.parametrize("name,N,K", [("qkv_gqa", 6144, 4096), ("gate_up", 28672, 4096), ("down", 4096, 14336)])
+def test_config4_w3a3_gemms_full_size(name, N, K):
+    print(f"case config4 gemm {name}", flush=True)
+    gemm_sampled(3, 4096, N, K, seed=N + K + 4)
+
+
+# ------------------------------------------------------------------ config 5
+@pytest.mark.timeout(600)
+def test_config5_site_full_batch():
+    cfg = synth.CONFIGS[5]
+    print("case config5 site (float64 SVD of an 8192 x 8192 matrix first)", flush=True)
+    U, M, _ = oracle_site(5, "A", cfg.r)
+    h = synth.residual(cfg)
+    out, codes, scales = run_site(to_dev(h, "bf16"), U, M, cfg.bits, "bf16")
+    check_site(h, U, M, "bf16", cfg.bits, out, codes, scales)
+
+
+@pytest.mark.parametrize("name,N,K", [("qkv_gqa", 10240, 8192), ("gate_up", 57344, 8192), ("down", 8192, 28672)])
+def test_config5_gemms_full_size(name, N, K):
+    print(f"case config5 gemm {name}", flush=True)
+    gemm_sampled(4, 4096, N, K, seed=N + K + 5)
