@@ -26,6 +26,10 @@ class RsqError(RuntimeError):
 
 
 def _load() -> C.CDLL:
+    # torch ships its own HIP runtime under the same soname; loading torch
+    # first makes librsq.so bind to that one copy (two runtimes in one
+    # process do not share the device).
+    import torch  # noqa: F401
     if not os.path.exists(LIB_PATH):
         raise ImportError(
             f"{LIB_PATH} is missing: build it with `python -m rotation_bit_post_amd.build` "

@@ -3,10 +3,10 @@
 //   acc[t, j] = sum_k a[t, k] w[j, k]            (int32, exact)
 //   y[t, j]   = (float(acc) * s_a[t]) * s_w[j]
 //
-// Packed tiles go from HBM/L2 to LDS unchanged (double buffered, one barrier
-// per 128-code k step) and are widened to int8 in registers right before
-// v_mfma_i32_32x32x32_i8. Widening only moves each code's bits to the top of
-// its byte, so the matrix core multiplies 16*a by 16*w (int4) or 32*a by
+// Packed tiles are loaded from HBM/L2, widened to int8 once per workgroup on
+// their way into LDS (double buffered, one barrier per 128-code k step) and
+// read back with 16-byte LDS loads straight into v_mfma_i32_32x32x32_i8.
+// Widening only moves each code's bits to the top of its byte, so the matrix core multiplies 16*a by 16*w (int4) or 32*a by
 // 32*w (int3); the epilogue shifts the exact accumulator back. With codes in
 // [-7, 7] and K <= 28672 the scaled sum stays below 2^29. The k order inside
 // a 32-code step is permuted the same way for both operands, which leaves the
@@ -22,17 +22,16 @@ namespace rsq {
 
 namespace {
 
-constexpr int kBK = 128;  // codes per k step
+constexpr int kBK = 128;       // codes per k step (4 matrix-core steps of 32)
+constexpr int kRowLds = 144;   // LDS bytes per row: 128 int8 + 16 pad (conflict-free 16-byte reads)
 
 template <int BITS> struct Fmt;
 template <> struct Fmt<4> {
-    static constexpr int kRowB = 64;     // packed bytes of 128 codes
-    static constexpr int kStride = 72;   // LDS row stride (bank-conflict-free 8-byte reads)
+    static constexpr int kGroupB = 16;   // packed bytes of 32 codes
     static constexpr int kShift = 8;     // (16 a)(16 w) = 256 a w
 };
 template <> struct Fmt<3> {
-    static constexpr int kRowB = 48;
-    static constexpr int kStride = 52;
+    static constexpr int kGroupB = 12;
     static constexpr int kShift = 10;    // (32 a)(32 w) = 1024 a w
 };
 
@@ -40,86 +39,199 @@ template <typename YT> __device__ __forceinline__ YT to_out(float v);
 template <> __device__ __forceinline__ float to_out<float>(float v) { return v; }
 template <> __device__ __forceinline__ uint16_t to_out<uint16_t>(float v) { return f32_to_bf16(v); }
 
-// Operand for one 32-code step s of a row held in LDS (lane half h = lane / 32).
-template <int BITS>
-__device__ __forceinline__ v4i lds_operand(const uint8_t *rowp, int s, int h) {
-    if constexpr (BITS == 4) {
-        const v2u x = *reinterpret_cast<const v2u *>(rowp + 16 * s + 8 * h);
-        return unpack_int4x16(x[0], x[1]);
-    } else {
-        const uint32_t *p = reinterpret_cast<const uint32_t *>(rowp + 12 * s);
-        return unpack_int3_half(p[0], p[1], p[2], h);
+// One group of 32 packed codes, as loaded from HBM.
+template <int BITS> struct Group;
+template <> struct Group<4> {
+    v4u x;
+    __device__ __forceinline__ void load(const uint8_t *p) { x = *reinterpret_cast<const v4u *>(p); }
+    __device__ __forceinline__ void keep_if(bool ok) {
+        x = v4u{ok ? x[0] : 0u, ok ? x[1] : 0u, ok ? x[2] : 0u, ok ? x[3] : 0u};
     }
+    // 32 int8 values (16 * code) in the order the matrix core consumes: lanes
+    // of half 0 take bytes 0-15, half 1 bytes 16-31.
+    __device__ __forceinline__ void widen(v4i &lo, v4i &hi) const {
+        lo = unpack_int4x16(x[0], x[1]);
+        hi = unpack_int4x16(x[2], x[3]);
+    }
+};
+template <> struct Group<3> {
+    uint32_t w0, w1, w2;
+    __device__ __forceinline__ void load(const uint8_t *p) {
+        const uint32_t *q = reinterpret_cast<const uint32_t *>(p);
+        w0 = q[0]; w1 = q[1]; w2 = q[2];
+    }
+    __device__ __forceinline__ void keep_if(bool ok) {
+        w0 = ok ? w0 : 0u; w1 = ok ? w1 : 0u; w2 = ok ? w2 : 0u;
+    }
+    __device__ __forceinline__ void widen(v4i &lo, v4i &hi) const {
+        lo = unpack_int3_half(w0, w1, w2, 0);
+        hi = unpack_int3_half(w0, w1, w2, 1);
+    }
+};
+
+// Tile order. The hardware deals workgroups round-robin to the 8 XCDs
+// (block b runs on XCD b % 8), each with its own L2. Block b is given a tile
+// from a contiguous range owned by its XCD, and tiles are numbered channel
+// tile major, so an XCD streams only its share of the weights and the
+// workgroups resident on it at one time share weight tiles.
+__device__ __forceinline__ int xcd_tile(int bid, int tiles) {
+    constexpr int kXcd = 8;
+    const int x = bid % kXcd, local = bid / kXcd;
+    const int base = tiles / kXcd, rem = tiles % kXcd;
+    return x * base + min(x, rem) + local;
 }
 
-template <int BITS, int BM, int BN, typename YT>
-__global__ __launch_bounds__(256) void qgemm_kernel(const uint8_t *__restrict__ A, const float *__restrict__ sa,
-                                                    int n, const uint8_t *__restrict__ W,
-                                                    const float *__restrict__ sw, int N, int K,
-                                                    YT *__restrict__ y, int64_t ld_y,
-                                                    int32_t *__restrict__ acc_out) {
+// BM tokens x BN channels per workgroup, WM x WN waves, each wave
+// (BM / WM) x (BN / WN) as TM x TN fragments of 32 x 32. Codes are widened to
+// int8 once, on their way into LDS; the inner loop is 16-byte LDS reads
+// straight into v_mfma_i32_32x32x32_i8.
+template <int BITS, int BM, int BN, int WM, int WN, int P>
+struct GemmTile {
     using F = Fmt<BITS>;
-    constexpr int PPR = F::kRowB / 16;             // 16-byte pieces per row per k step
-    constexpr int PIECES = (BM + BN) * PPR;
-    constexpr int PPT = (PIECES + 255) / 256;      // pieces per thread
-    constexpr int TM = BM / 64, TN = BN / 64;      // 32x32 fragments per wave (2 x 2 waves)
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2][(BM + BN) * F::kStride];
+    static constexpr int NT = WM * WN * 64;
+    static constexpr int GPR = kBK / 32;                  // code groups per row per k step
+    static constexpr int GROUPS = (BM + BN) * GPR;
+    static constexpr int GPT = (GROUPS + NT - 1) / NT;    // groups per thread
+    static constexpr int TM = BM / WM / 32, TN = BN / WN / 32;
+    static constexpr int LDS_BYTES = 2 * (BM + BN) * kRowLds;
 
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int wm = wv >> 1, wn = wv & 1;
+    // Whether every thread's i-th group lies in the A rows (0), the W rows (1)
+    // or either (2); known at compile time for the shapes used.
+    static constexpr int side(int i) {
+        return NT * (i + 1) <= BM * GPR ? 0 : (NT * i >= BM * GPR ? 1 : 2);
+    }
+
+    // Main loop. FAST: the tile lies inside both matrices and K is a multiple
+    // of 128, so loads need no clamping and no masking, and their addresses
+    // are a per-thread 32-bit offset from a workgroup-uniform base.
+    template <bool FAST>
+    __device__ __forceinline__ static void run(uint8_t *lds, const uint8_t *A, const uint8_t *W, int n, int N,
+                                               int K, int bm0, int bn0, v16i (&acc)[TM][TN]) {
+        const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+        const int wm = wv / WN, wn = wv % WN;
+        const int h = lane >> 5, l32 = lane & 31;
+        const uint32_t rb = static_cast<uint32_t>(K) * BITS / 8;  // packed row bytes
+        const int nkt = (K + kBK - 1) / kBK;
+        const uint8_t *abase = A + static_cast<size_t>(bm0) * rb;
+        const uint8_t *wbase = W + static_cast<size_t>(bn0) * rb;
+
+        uint32_t goff[GPT];
+        int ldst[GPT], gk[GPT];
+        bool gvalid[GPT], isa[GPT];
+#pragma unroll
+        for (int i = 0; i < GPT; ++i) {
+            const int g = min(tid + NT * i, GROUPS - 1);  // threads past the end redo the last group
+            const int row = g / GPR, part = g % GPR;      // LDS row: A rows first, then W rows
+            isa[i] = row < BM;
+            const int r = isa[i] ? row : row - BM;
+            gvalid[i] = isa[i] ? bm0 + r < n : bn0 + r < N;
+            goff[i] = (gvalid[i] ? static_cast<uint32_t>(r) : 0u) * rb + F::kGroupB * part;
+            ldst[i] = row * kRowLds + 32 * part;
+            gk[i] = 32 * part;
+        }
+        auto src = [&](int i) -> const uint8_t * {
+            if (side(i) == 0) return abase;
+            if (side(i) == 1) return wbase;
+            return isa[i] ? abase : wbase;
+        };
+
+        // P k steps of packed codes are in flight in registers (a ring of P
+        // slots). In the main loop no load is behind a branch, so the compiler
+        // keeps the newer slots' loads outstanding while it drains the oldest.
+        // Outside FAST, addresses are clamped into the matrix and rows or k
+        // groups outside it are zeroed when the slot is written to LDS.
+        Group<BITS> stage[P][GPT];
+        const int last_group_k = ((K - 1) / 32) * 32;    // k of the last 32-code group of a row
+        auto load_tile = [&](int kt, Group<BITS> *st) {
+            kt = min(kt, nkt - 1);
+#pragma unroll
+            for (int i = 0; i < GPT; ++i) {
+                if constexpr (FAST) {
+                    st[i].load(src(i) + goff[i] + static_cast<uint32_t>(kt) * (GPR * F::kGroupB));
+                } else {
+                    const int k = min(kt * kBK + gk[i] - gk[i] % 32, last_group_k);
+                    st[i].load(src(i) + goff[i] - (gk[i] / 32) * F::kGroupB + static_cast<uint32_t>(k / 32) * F::kGroupB);
+                }
+            }
+        };
+        auto store_tile = [&](int kt, int buf, Group<BITS> *st) {
+#pragma unroll
+            for (int i = 0; i < GPT; ++i) {
+                if constexpr (!FAST) st[i].keep_if(gvalid[i] && kt * kBK + gk[i] < K);
+                v4i lo, hi;
+                st[i].widen(lo, hi);
+                v4i *dst = reinterpret_cast<v4i *>(lds + buf * (LDS_BYTES / 2) + ldst[i]);
+                dst[0] = lo;
+                dst[1] = hi;
+            }
+        };
+
+        const int arow = (wm * (BM / WM) + l32) * kRowLds + 16 * h;
+        const int wrow = (BM + wn * (BN / WN) + l32) * kRowLds + 16 * h;
+        // operands of one 32-code step, double buffered: step s + 1 is read
+        // from LDS while the matrix cores work on step s
+        v4i ao[2][TM], wo[2][TN];
+        auto read_ops = [&](const uint8_t *lb, int s, int slot) {
+#pragma unroll
+            for (int i = 0; i < TM; ++i) ao[slot][i] = *reinterpret_cast<const v4i *>(lb + arow + 32 * i * kRowLds + 32 * s);
+#pragma unroll
+            for (int j = 0; j < TN; ++j) wo[slot][j] = *reinterpret_cast<const v4i *>(lb + wrow + 32 * j * kRowLds + 32 * s);
+        };
+        // one k step: refill slot u with step kt + P, multiply step kt from
+        // LDS, then write step kt + 1 (slot u + 1) to the other LDS buffer
+        auto step = [&](int kt, int u) {
+            load_tile(kt + P, stage[u]);
+            __builtin_amdgcn_sched_barrier(0);  // issue the loads before this step's work
+            const uint8_t *lb = lds + (kt & 1) * (LDS_BYTES / 2);
+            read_ops(lb, 0, 0);
+#pragma unroll
+            for (int s = 0; s < kBK / 32; ++s) {
+                if (s + 1 < kBK / 32) read_ops(lb, s + 1, (s + 1) & 1);
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+#pragma unroll
+                    for (int j = 0; j < TN; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ao[s & 1][i], wo[s & 1][j], acc[i][j], 0, 0, 0);
+            }
+            store_tile(kt + 1, (kt + 1) & 1, stage[(u + 1) % P]);
+            __syncthreads();
+        };
+
+#pragma unroll
+        for (int u = 0; u < P; ++u) load_tile(u, stage[u]);
+        store_tile(0, 0, stage[0]);
+        __syncthreads();
+        int kt = 0;
+        for (; kt + P <= nkt; kt += P) {
+#pragma unroll
+            for (int u = 0; u < P; ++u) step(kt + u, u);
+        }
+#pragma unroll
+        for (int u = 0; u < P - 1; ++u)
+            if (kt + u < nkt) step(kt + u, u);
+    }
+};
+
+template <int BITS, int BM, int BN, int WM, int WN, int P, typename YT>
+__global__ __launch_bounds__(WM * WN * 64) void qgemm_kernel(const uint8_t *__restrict__ A,
+                                                             const float *__restrict__ sa, int n,
+                                                             const uint8_t *__restrict__ W,
+                                                             const float *__restrict__ sw, int N, int K,
+                                                             YT *__restrict__ y, int64_t ld_y,
+                                                             int32_t *__restrict__ acc_out) {
+    using T = GemmTile<BITS, BM, BN, WM, WN, P>;
+    using F = Fmt<BITS>;
+    constexpr int TM = T::TM, TN = T::TN;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[T::LDS_BYTES];
+
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int wm = wv / WN, wn = wv % WN;
     const int h = lane >> 5, l32 = lane & 31;
     const int mt = (n + BM - 1) / BM;
-    const int bm0 = (blockIdx.x % mt) * BM;
-    const int bn0 = (blockIdx.x / mt) * BN;
-    const size_t rb = static_cast<size_t>(K) * BITS / 8;  // packed row bytes
-    const int nkt = (K + kBK - 1) / kBK;
-
-    v4u stage[PPT];
-    auto load_tile = [&](int kt) {
-        const int kvalid = min(kBK, K - kt * kBK);          // codes of this step inside the row
-        const int bvalid = kvalid * BITS / 8;                // bytes
-#pragma unroll
-        for (int i = 0; i < PPT; ++i) {
-            const int p = tid + 256 * i;
-            v4u val = v4u{0, 0, 0, 0};
-            if (p < PIECES) {
-                const bool is_a = p < BM * PPR;
-                const int q = is_a ? p : p - BM * PPR;
-                const int row = q / PPR, part = q % PPR;
-                const int grow = (is_a ? bm0 : bn0) + row;
-                const bool rvalid = is_a ? grow < n : grow < N;
-                const uint8_t *src = (is_a ? A : W) + static_cast<size_t>(grow) * rb + static_cast<size_t>(kt) * F::kRowB + 16 * part;
-                if (rvalid) {
-                    // int3 rows are only 4-byte aligned when K is not a multiple of 128
-                    if (16 * part + 16 <= bvalid && (BITS == 4 || (rb & 15) == 0)) {
-                        val = *reinterpret_cast<const v4u *>(src);
-                    } else {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            if (16 * part + 4 * e + 4 <= bvalid) val[e] = reinterpret_cast<const uint32_t *>(src)[e];
-                    }
-                }
-            }
-            stage[i] = val;
-        }
-    };
-    auto store_tile = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < PPT; ++i) {
-            const int p = tid + 256 * i;
-            if (p < PIECES) {
-                const int row = p / PPR, part = p % PPR;  // A rows then W rows, contiguous in LDS
-                uint32_t *dst = reinterpret_cast<uint32_t *>(&lds[buf][row * F::kStride + 16 * part]);
-                if constexpr (F::kStride % 8 == 0) {
-                    reinterpret_cast<v2u *>(dst)[0] = v2u{stage[i][0], stage[i][1]};
-                    reinterpret_cast<v2u *>(dst)[1] = v2u{stage[i][2], stage[i][3]};
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) dst[e] = stage[i][e];
-                }
-            }
-        }
-    };
+    const int tiles = mt * ((N + BN - 1) / BN);
+    const int tile = xcd_tile(blockIdx.x, tiles);
+    const int bm0 = (tile % mt) * BM;
+    const int bn0 = (tile / mt) * BN;
 
     v16i acc[TM][TN];
 #pragma unroll
@@ -129,44 +241,22 @@ __global__ __launch_bounds__(256) void qgemm_kernel(const uint8_t *__restrict__ 
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0;
 
-    load_tile(0);
-    store_tile(0);
-    __syncthreads();
-    for (int kt = 0; kt < nkt; ++kt) {
-        const int buf = kt & 1;
-        if (kt + 1 < nkt) load_tile(kt + 1);
-        const uint8_t *la = &lds[buf][0];
-        const uint8_t *lw = &lds[buf][BM * F::kStride];
-#pragma unroll
-        for (int s = 0; s < kBK / 32; ++s) {
-            v4i ao[TM], wo[TN];
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-                ao[i] = lds_operand<BITS>(la + (wm * (BM / 2) + 32 * i + l32) * F::kStride, s, h);
-#pragma unroll
-            for (int j = 0; j < TN; ++j)
-                wo[j] = lds_operand<BITS>(lw + (wn * (BN / 2) + 32 * j + l32) * F::kStride, s, h);
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-#pragma unroll
-                for (int j = 0; j < TN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ao[i], wo[j], acc[i][j], 0, 0, 0);
-        }
-        if (kt + 1 < nkt) store_tile(buf ^ 1);
-        __syncthreads();
-    }
+    if (bm0 + BM <= n && bn0 + BN <= N && K % kBK == 0)
+        T::template run<true>(lds, A, W, n, N, K, bm0, bn0, acc);
+    else
+        T::template run<false>(lds, A, W, n, N, K, bm0, bn0, acc);
 
     // epilogue: lane holds channel l32 of each fragment and tokens 8(v/4) + 4h + v%4
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
-        const int ch = bn0 + wn * (BN / 2) + 32 * j + l32;
+        const int ch = bn0 + wn * (BN / WN) + 32 * j + l32;
         const bool cvalid = ch < N;
         const float swj = cvalid ? sw[ch] : 0.0f;
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                const int tok = bm0 + wm * (BM / 2) + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
+                const int tok = bm0 + wm * (BM / WM) + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
                 if (cvalid && tok < n) {
                     const int a = acc[i][j][v] >> F::kShift;
                     const float val = (static_cast<float>(a) * sa[tok]) * swj;
@@ -178,21 +268,27 @@ __global__ __launch_bounds__(256) void qgemm_kernel(const uint8_t *__restrict__ 
     }
 }
 
-template <int BITS, int BM, int BN, typename YT>
+template <int BITS, int BM, int BN, int WM, int WN, typename YT, int P = 2>
 hipError_t launch_t(const uint8_t *a, const float *sa, int64_t n, const uint8_t *w, const float *sw, int64_t N,
                     int64_t K, void *y, int64_t ld_y, int32_t *acc_out, hipStream_t s) {
     const int64_t mt = (n + BM - 1) / BM, nt = (N + BN - 1) / BN;
-    hipLaunchKernelGGL((qgemm_kernel<BITS, BM, BN, YT>), dim3(static_cast<unsigned>(mt * nt)), dim3(256), 0, s,
-                       a, sa, static_cast<int>(n), w, sw, static_cast<int>(N), static_cast<int>(K),
-                       static_cast<YT *>(y), ld_y, acc_out);
+    hipLaunchKernelGGL((qgemm_kernel<BITS, BM, BN, WM, WN, P, YT>), dim3(static_cast<unsigned>(mt * nt)),
+                       dim3(WM * WN * 64), 0, s, a, sa, static_cast<int>(n), w, sw, static_cast<int>(N),
+                       static_cast<int>(K), static_cast<YT *>(y), ld_y, acc_out);
     return hipGetLastError();
 }
 
+// Tile shape by problem size (measured on MI355X: 256 x 128 tiles with 8
+// waves lead on the layer shapes; smaller tiles keep small batches spread
+// over the CUs).
 template <int BITS, typename YT>
 hipError_t launch_b(const uint8_t *a, const float *sa, int64_t n, const uint8_t *w, const float *sw, int64_t N,
                     int64_t K, void *y, int64_t ld_y, int32_t *acc_out, hipStream_t s) {
-    if (n <= 64) return launch_t<BITS, 64, 64, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, s);
-    return launch_t<BITS, 128, 128, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, s);
+    if (n <= 32) return launch_t<BITS, 32, 128, 1, 4, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, s);
+    if (n <= 64) return launch_t<BITS, 64, 128, 2, 2, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, s);
+    const int64_t tiles = ((n + 255) / 256) * ((N + 127) / 128);
+    if (n >= 256 && tiles >= 200) return launch_t<BITS, 256, 128, 4, 2, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, s);
+    return launch_t<BITS, 128, 128, 2, 2, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, s);
 }
 
 }  // namespace
