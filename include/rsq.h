@@ -98,7 +98,9 @@ rsq_status rsq_subspace_correct(const void *h_in, void *h_out, int h_dtype,
 /*
  * Per-token symmetric activation quantisation (the A4 / A3 settings of
  * zh 4 and fr 4), with optional RMSNorm first (flags & RSQ_QA_RMSNORM):
- *   inv   = float32(1 / sqrt(mean_k(x^2) + eps))       (sum of squares in float64)
+ *   inv   = float32(1 / sqrt(mean_k(x^2) + eps))       (sum of squares in float64;
+ *           within a few float32 ulps of the exact sum: the summation
+ *           order is the kernel's)
  *   a     = (x * inv) * w    (float32; w = norm_w, or 1 if norm_w is NULL);
  *           without the flag a = x
  *   s     = max_k |a| / qmax                           (qmax = 2^(bits-1) - 1)
@@ -115,7 +117,11 @@ rsq_status rsq_quant_act(const void *x, int x_dtype, int64_t n, int64_t k, int64
 /*
  * Correction, RMSNorm and quantisation in one pass over the residual:
  * rsq_subspace_correct followed by rsq_quant_act(RSQ_QA_RMSNORM) on the
- * rounded h_out, with identical results (the norm reads h_out as stored).
+ * rounded h_out (the norm reads h_out as stored). h_out is identical to
+ * rsq_subspace_correct's; the sum of squares is taken in another order
+ * (bfloat16 squares summed by 8 in float32, exactly per product, then in
+ * float64), so scales may differ from rsq_quant_act's by a few ulps and codes
+ * only where a / s lies that close to a rounding tie.
  * h_in, h_out: contiguous rows (stride d).
  */
 rsq_status rsq_correct_quant(const void *h_in, void *h_out, int h_dtype, int64_t n, int64_t d,

@@ -32,7 +32,7 @@ def _load() -> C.CDLL:
     import torch  # noqa: F401
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"{LIB_PATH} is missing: build it with `python -m rotation_bit_post_amd.build` "
+            f"{LIB_PATH} is missing: build it with `python rotation_bit_post_amd/build.py` "
             "(there is no fallback implementation)")
     lib = C.CDLL(LIB_PATH)
     vp, i64, i32, f32, sz = C.c_void_p, C.c_int64, C.c_int, C.c_float, C.c_size_t

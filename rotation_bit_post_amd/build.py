@@ -1,6 +1,9 @@
 """Build librsq.so (the HIP kernels and the C ABI) in place, for gfx950.
 
-    python -m rotation_bit_post_amd.build      # or build() from Python
+    python rotation_bit_post_amd/build.py      # or build() from Python
+
+It is run as a file (not through the package) so that a stale or missing
+library never stops a rebuild: importing the package loads the library.
 
 The library is compiled every time this runs; the objects go to
 ``_build/`` at the repository root and the shared library next to this file.

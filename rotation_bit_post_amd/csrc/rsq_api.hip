@@ -41,7 +41,7 @@ rsq_status check_site(int64_t d, int r) {
     RSQ_CHECK(r <= d, RSQ_ERR_INVALID_ARG, "r = %d exceeds d = %lld", r, (long long)d);
     RSQ_CHECK(d <= (1 << 20), RSQ_ERR_UNSUPPORTED, "d = %lld too large", (long long)d);
     int nw = 0, cpw = 0;
-    RSQ_CHECK(rsq::correct_geometry(d, &nw, &cpw), RSQ_ERR_UNSUPPORTED,
+    RSQ_CHECK(rsq::correct_geometry(d, false, &nw, &cpw), RSQ_ERR_UNSUPPORTED,
               "d = %lld: d/32 must split into at most 8 waves of 1, 2, 4, 8, 16 or 32 chunks", (long long)d);
     return RSQ_OK;
 }
@@ -57,6 +57,10 @@ rsq_status check_correct_args(const void *h_in, const void *h_out, int h_dtype, 
     RSQ_CHECK(n >= 0, RSQ_ERR_INVALID_ARG, "n = %lld is negative", (long long)n);
     rsq_status st = check_site(d, r);
     if (st != RSQ_OK) return st;
+    int nw = 0, cpw = 0;
+    RSQ_CHECK(h_dtype != RSQ_F32 || rsq::correct_geometry(d, true, &nw, &cpw), RSQ_ERR_UNSUPPORTED,
+              "d = %lld: a float32 residual needs d/32 split into at most 8 waves of at most 16 chunks",
+              (long long)d);
     RSQ_CHECK(ld_h >= d, RSQ_ERR_INVALID_ARG, "ld_h = %lld < d = %lld", (long long)ld_h, (long long)d);
     RSQ_CHECK((ld_h * (int64_t)dtype_size(h_dtype)) % 16 == 0, RSQ_ERR_INVALID_ARG,
               "row stride of %lld bytes is not a multiple of 16", (long long)(ld_h * (int64_t)dtype_size(h_dtype)));

@@ -5,18 +5,22 @@
 //   c = p M            transform inside it (M = R_sub - I_r)
 //   h' = h + c U^T     reprojection added to the residual
 // Folding M into the second basis, c U^T = p V^T with V = U M^T, leaves two
-// skinny contractions. Both run on the bf16 matrix cores with a hi/lo split
-// of the float32 operands (about 2^-17 relative each) and float32
+// skinny contractions, both on the bf16 matrix cores with float32
 // accumulation; the reprojection's accumulator starts at h, so the residual
-// add costs nothing.
+// add costs nothing. A bfloat16 residual takes bf16 operands (h is exact in
+// bf16; U, V and p carry 2^-9 relative rounding, far below the rounding of
+// h' itself). A float32 residual also takes the bf16 remainders (hi + lo
+// splits, about 2^-17 relative per operand).
 //
-// Work split: a workgroup owns 16 tokens (the matrix-core N dimension) and
-// up to 8 waves (two per SIMD, 256 registers each); each wave owns some 32-column chunks of d and keeps its
-// slice of the 16 rows in registers from the load until the store, so the
-// residual crosses HBM once in and once out. Lane l holds token (l % 16) and
-// columns 32c + 8(l / 16) .. +7 of chunk c: the B operand of the projection
-// (k-slot e = column 32c + 8g + e) and, by the row order chosen for V, also
-// the accumulator layout of the reprojection.
+// Work split: a workgroup owns tb (8 or 16) tokens - the matrix-core N
+// dimension is 16, and 8 is used when 16 would leave compute units idle -
+// and up to 8 waves (two per SIMD); each wave owns some 32-column chunks of d
+// and keeps its slice of the rows in registers from the load until the
+// store, so the residual crosses HBM once in and once out. The basis
+// operands stream from L2 through a ring of PD chunks per wave. Lane l holds
+// token (l % 16) and columns 32c + 8(l / 16) .. +7 of chunk c: the B operand
+// of the projection (k-slot e = column 32c + 8g + e) and, by the row order
+// chosen for V, also the accumulator layout of the reprojection.
 #include "rsq_device.h"
 #include "rsq_internal.h"
 
@@ -24,27 +28,28 @@ namespace rsq {
 
 namespace {
 
-constexpr int kTok = 16;        // tokens per workgroup
 constexpr int kMaxWaves = 8;
 
 // ------------------------------------------------------------ site layout
-// U part: [chunk c][j-block jb (16 wide)][hi|lo][lane][8]: lane l, element e
-//         holds U[32c + 8(l/16) + e][16 jb + l%16].
-// V part: [chunk c][row-block b][k-block kk (32 wide)][hi|lo][lane][8]: lane l,
-//         element e holds V[d][32 kk + 8(l/16) + e] with
-//         d = 32c + 8((l%16)/4) + 4b + (l%16)%4.
-__device__ __forceinline__ size_t u_index(int c, int jb, int hl, int lane, int njb) {
-    return ((static_cast<size_t>(c) * njb + jb) * 2 + hl) * 512 + lane * 8;
+// Four parts of d * r_pad bf16 each: U hi, V hi, U lo, V lo (a bf16 residual
+// reads only the first two).
+// U part: [chunk c][j-block jb (16 wide)][lane][8]: lane l, element e holds
+//         U[32c + 8(l/16) + e][16 jb + l%16].
+// V part: [chunk c][row-block b][k-block kk (32 wide)][lane][8]: lane l,
+//         element e holds V[dd][32 kk + 8(l/16) + e] with
+//         dd = 32c + 8((l%16)/4) + 4b + (l%16)%4.
+__device__ __forceinline__ size_t u_index(int c, int jb, int lane, int njb) {
+    return ((static_cast<size_t>(c) * njb + jb) * 64 + lane) * 8;
 }
-__device__ __forceinline__ size_t v_index(int c, int b, int kk, int hl, int lane, int nkk) {
-    return (((static_cast<size_t>(c) * 2 + b) * nkk + kk) * 2 + hl) * 512 + lane * 8;
+__device__ __forceinline__ size_t v_index(int c, int b, int kk, int lane, int r32) {
+    return (((static_cast<size_t>(c) * 2 + b) * r32 + kk) * 64 + lane) * 8;
 }
 
+// One thread per (part, position); position i of a part is its index above.
 __global__ void site_prepare_kernel(const float *__restrict__ U, const float *__restrict__ M, int d, int r,
                                     int r_pad, uint16_t *__restrict__ site) {
     const int njb = r_pad / 16, nkk = r_pad / 32;
-    const size_t half = static_cast<size_t>(d) * r_pad * 2;  // elements of the U part (hi + lo)
-    const size_t per = static_cast<size_t>(d) * r_pad;       // (chunk, block, lane, e) positions
+    const size_t per = static_cast<size_t>(d) * r_pad;
     size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
     if (i >= 2 * per) return;
     const bool is_v = i >= per;
@@ -52,14 +57,11 @@ __global__ void site_prepare_kernel(const float *__restrict__ U, const float *__
     const int e = static_cast<int>(i % 8);
     const int lane = static_cast<int>((i / 8) % 64);
     const size_t blk = i / 512;  // U: c * njb + jb ; V: (c * 2 + b) * nkk + kk
+    float val;
     if (!is_v) {
         const int jb = static_cast<int>(blk % njb), c = static_cast<int>(blk / njb);
         const int row = 32 * c + 8 * (lane / 16) + e, col = 16 * jb + lane % 16;
-        const float u = col < r ? U[static_cast<size_t>(row) * r + col] : 0.0f;
-        uint16_t hi, lo;
-        split_bf16(u, hi, lo);
-        site[u_index(c, jb, 0, lane, njb) + e] = hi;
-        site[u_index(c, jb, 1, lane, njb) + e] = lo;
+        val = col < r ? U[static_cast<size_t>(row) * r + col] : 0.0f;
     } else {
         const int kk = static_cast<int>(blk % nkk);
         const int b = static_cast<int>((blk / nkk) % 2), c = static_cast<int>(blk / nkk / 2);
@@ -70,11 +72,13 @@ __global__ void site_prepare_kernel(const float *__restrict__ U, const float *__
         if (col < r)
             for (int m = 0; m < r; ++m)
                 v += static_cast<double>(U[static_cast<size_t>(row) * r + m]) * static_cast<double>(M[static_cast<size_t>(col) * r + m]);
-        const uint16_t hi = f32_to_bf16(static_cast<float>(v));
-        const uint16_t lo = f32_to_bf16(static_cast<float>(v - static_cast<double>(bf16_to_f32(hi))));
-        site[half + v_index(c, b, kk, 0, lane, nkk) + e] = hi;
-        site[half + v_index(c, b, kk, 1, lane, nkk) + e] = lo;
+        val = static_cast<float>(v);
     }
+    uint16_t hi, lo;
+    split_bf16(val, hi, lo);
+    const size_t base = is_v ? per : 0;
+    site[base + i] = hi;
+    site[2 * per + base + i] = lo;
 }
 
 // ------------------------------------------------------ residual storage
@@ -88,11 +92,18 @@ template <> struct Row8<uint16_t> {  // bfloat16: 8 values in 16 bytes
         const uint32_t w = raw[e >> 1];
         return __uint_as_float((e & 1) ? (w & 0xFFFF0000u) : (w << 16));
     }
-    __device__ __forceinline__ void set(int e, float f) {  // rounds to nearest even
-        const uint32_t b = f32_to_bf16(f);
-        uint32_t w = raw[e >> 1];
-        w = (e & 1) ? ((w & 0xFFFFu) | (b << 16)) : ((w & 0xFFFF0000u) | b);
-        raw[e >> 1] = w;
+    // elements 4b .. 4b+3, rounded to nearest even
+    __device__ __forceinline__ void set4(int b, v4f x) {
+        raw[2 * b] = pk_bf16(x[0], x[1]);
+        raw[2 * b + 1] = pk_bf16(x[2], x[3]);
+    }
+    // sum of squares of the 8 stored values: bf16 products are exact in
+    // float32; float32 adds within the row piece, float64 across pieces
+    __device__ __forceinline__ double sumsq() const {
+        float s = 0.0f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) s = __builtin_amdgcn_fdot2_f32_bf16(as_v2bf(raw[q]), as_v2bf(raw[q]), s, false);
+        return static_cast<double>(s);
     }
     __device__ __forceinline__ void operands(v8bf &hi, v8bf &lo) const { hi = as_v8bf(raw); (void)lo; }
     // Hide the value from common-subexpression elimination, so unpacked copies
@@ -112,7 +123,13 @@ template <> struct Row8<float> {  // float32: 8 values in 32 bytes
     }
     __device__ __forceinline__ void zero() { a = v4f{0, 0, 0, 0}; b = a; }
     __device__ __forceinline__ float get(int e) const { return e < 4 ? a[e] : b[e - 4]; }
-    __device__ __forceinline__ void set(int e, float f) { if (e < 4) a[e] = f; else b[e - 4] = f; }
+    __device__ __forceinline__ void set4(int blk, v4f x) { if (blk == 0) a = x; else b = x; }
+    __device__ __forceinline__ double sumsq() const {  // float64 products and adds
+        double s = 0.0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s = fma(static_cast<double>(get(e)), static_cast<double>(get(e)), s);
+        return s;
+    }
     __device__ __forceinline__ void operands(v8bf &hi, v8bf &lo) const {
         v4u h, l;
 #pragma unroll
@@ -132,155 +149,190 @@ template <> struct Row8<float> {  // float32: 8 values in 32 bytes
 
 __device__ __forceinline__ v8bf load_op(const uint16_t *p) { return as_v8bf(*reinterpret_cast<const v4u *>(p)); }
 
+
 // ------------------------------------------------------------ main kernel
 // T: uint16_t (bf16) or float. CPW: 32-column chunks per wave. R32: r_pad / 32.
 template <typename T, int CPW, int R32, bool QUANT>
-__global__ __launch_bounds__(512) void correct_kernel(
+__global__ __launch_bounds__(64 * kMaxWaves) void correct_kernel(
     const T *__restrict__ h_in, T *__restrict__ h_out, int64_t n, int d, int64_t ld_h,
-    const uint16_t *__restrict__ site, int nw, const float *__restrict__ norm_w, float eps, int bits,
+    const uint16_t *__restrict__ site, int tb, const float *__restrict__ norm_w, float eps, int bits,
     uint8_t *__restrict__ codes, float *__restrict__ scales) {
-    constexpr int NJB = 2 * R32;  // 16-wide j blocks
-    __shared__ float red[kMaxWaves][kTok][33];
-    __shared__ __attribute__((aligned(16))) uint16_t pbuf[2][kTok][R32 * 32 + 8];
-    __shared__ double ssq[kMaxWaves][kTok];
-    __shared__ float amx[kMaxWaves][kTok];
+    constexpr bool SPLIT = Row8<T>::kSplit;
+    constexpr int NJB = 2 * R32;               // 16-wide j blocks of the projection
+    constexpr int RPS = 32 * R32 + 4;          // LDS row stride of the partial projections (floats)
+    // chunks of basis operands in flight per wave: 8 (64 registers) unless
+    // the residual slice or the operands are large
+    constexpr int HREGS = CPW * 2 * static_cast<int>(sizeof(T));
+    constexpr int PD0 = (HREGS >= 128 ? 4 : 8) / (SPLIT ? 2 : 1) / R32;
+    constexpr int PD = CPW < PD0 ? CPW : PD0;
+    constexpr int NL = SPLIT ? PD : 1;
+    __shared__ __attribute__((aligned(16))) float lp[kMaxWaves * 16 * RPS];
+    __shared__ double lss[kMaxWaves * 16];
+    __shared__ float lam[kMaxWaves * 16];
+    __shared__ float lwm[kMaxWaves * 16];
 
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int nw = blockDim.x >> 6;
+    // the wave index is uniform: keeping it in a scalar register keeps every
+    // per-chunk offset below scalar as well
+    const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+    const int lane = threadIdx.x & 63;
     const int g = lane >> 4, tl = lane & 15;
-    const int64_t t = static_cast<int64_t>(blockIdx.x) * kTok + tl;
-    const bool valid = t < n;
-    const size_t vbase = static_cast<size_t>(d) * R32 * 32 * 2;  // start of the V part
+    const int64_t t0 = static_cast<int64_t>(blockIdx.x) * tb;
+    const int64_t t = t0 + tl;
+    const bool valid = tl < tb && t < n;
+    // lanes without a token of their own read the block's first row (in
+    // bounds, already being fetched) and store nothing
+    const int64_t tload = valid ? t : t0;
+    const size_t per = static_cast<size_t>(d) * 32 * R32;
+    const uint16_t *u_hi = site, *v_hi = site + per, *u_lo = site + 2 * per, *v_lo = site + 3 * per;
+    (void)u_lo;
+    (void)v_lo;
 
-    // 1. residual slice -> registers
+    // 1. residual slice -> registers; every load in flight at once
     Row8<T> hr[CPW];
 #pragma unroll
-    for (int m = 0; m < CPW; ++m) {
-        const int c = w + nw * m;
-        if (valid) hr[m].load(h_in + t * ld_h + 32 * c + 8 * g);
-        else hr[m].zero();
-    }
+    for (int m = 0; m < CPW; ++m) hr[m].load(h_in + tload * ld_h + 32 * (w + nw * m) + 8 * g);
 
-    // 2. projection: P^T (r_pad x 16 tokens) partial over this wave's chunks.
-    //    Operands of chunk m + 1 are loaded while chunk m is multiplied.
+    // 2. projection: P^T (r_pad x 16 tokens), partial over this wave's chunks
     v4f acc[NJB];
 #pragma unroll
     for (int jb = 0; jb < NJB; ++jb) acc[jb] = v4f{0, 0, 0, 0};
-    v8bf uh[2][NJB], ul[2][NJB];
+    v8bf uh[PD][NJB], ul[NL][NJB];
 #pragma unroll
-    for (int jb = 0; jb < NJB; ++jb) {
-        uh[0][jb] = load_op(site + u_index(w, jb, 0, lane, NJB));
-        ul[0][jb] = load_op(site + u_index(w, jb, 1, lane, NJB));
-    }
+    for (int p = 0; p < PD; ++p)
+#pragma unroll
+        for (int jb = 0; jb < NJB; ++jb) {
+            uh[p][jb] = load_op(u_hi + u_index(w + nw * p, jb, lane, NJB));
+            if constexpr (SPLIT) ul[p % NL][jb] = load_op(u_lo + u_index(w + nw * p, jb, lane, NJB));
+        }
 #pragma unroll
     for (int m = 0; m < CPW; ++m) {
-        const int cur = m & 1;
-        if (m + 1 < CPW) {
-            const int cn = w + nw * (m + 1);
-#pragma unroll
-            for (int jb = 0; jb < NJB; ++jb) {
-                uh[cur ^ 1][jb] = load_op(site + u_index(cn, jb, 0, lane, NJB));
-                ul[cur ^ 1][jb] = load_op(site + u_index(cn, jb, 1, lane, NJB));
-            }
-        }
+        const int sl = m % PD;
         v8bf bh, bl;
         hr[m].operands(bh, bl);
 #pragma unroll
         for (int jb = 0; jb < NJB; ++jb) {
-            acc[jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(uh[cur][jb], bh, acc[jb], 0, 0, 0);
-            acc[jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ul[cur][jb], bh, acc[jb], 0, 0, 0);
-            if constexpr (Row8<T>::kSplit)
-                acc[jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(uh[cur][jb], bl, acc[jb], 0, 0, 0);
+            acc[jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(uh[sl][jb], bh, acc[jb], 0, 0, 0);
+            if constexpr (SPLIT) {
+                acc[jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ul[sl % NL][jb], bh, acc[jb], 0, 0, 0);
+                acc[jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(uh[sl][jb], bl, acc[jb], 0, 0, 0);
+            }
         }
-        __builtin_amdgcn_sched_barrier(0);  // one chunk of operands in flight at a time
-    }
-
-    // first reprojection operands, loaded before the reduction so their
-    // latency overlaps it (steps are (chunk m, row block b), 2 per chunk)
-    v8bf vh[2][R32], vl[2][R32];
+        if (m + PD < CPW) {
+            const int cn = w + nw * (m + PD);
 #pragma unroll
-    for (int kk = 0; kk < R32; ++kk) {
-        vh[0][kk] = load_op(site + vbase + v_index(w, 0, kk, 0, lane, R32));
-        vl[0][kk] = load_op(site + vbase + v_index(w, 0, kk, 1, lane, R32));
-    }
-
-    // 3. sum the partial projections over waves, 32 columns of P at a time,
-    //    and keep P as bf16 hi + lo in LDS
-#pragma unroll
-    for (int kk = 0; kk < R32; ++kk) {
-#pragma unroll
-        for (int jh = 0; jh < 2; ++jh)
-#pragma unroll
-            for (int v = 0; v < 4; ++v) red[w][tl][16 * jh + 4 * g + v] = acc[2 * kk + jh][v];
-        __syncthreads();
-        for (int idx = threadIdx.x; idx < kTok * 32; idx += blockDim.x) {
-            const int tok = idx >> 5, j = idx & 31;
-            float s = 0.0f;
-            for (int ww = 0; ww < nw; ++ww) s += red[ww][tok][j];
-            uint16_t hi, lo;
-            split_bf16(s, hi, lo);
-            pbuf[0][tok][32 * kk + j] = hi;
-            pbuf[1][tok][32 * kk + j] = lo;
+            for (int jb = 0; jb < NJB; ++jb) {
+                uh[sl][jb] = load_op(u_hi + u_index(cn, jb, lane, NJB));
+                if constexpr (SPLIT) ul[sl % NL][jb] = load_op(u_lo + u_index(cn, jb, lane, NJB));
+            }
         }
-        __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
     }
 
-    // 4. reprojection + residual: C (16 rows of d x 16 tokens) starts at h
+    // first reprojection operands, in flight during the reduction below
+    v8bf vh[PD][2][R32], vl[NL][2][R32];
+#pragma unroll
+    for (int p = 0; p < PD; ++p)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int kk = 0; kk < R32; ++kk) {
+                vh[p][b][kk] = load_op(v_hi + v_index(w + nw * p, b, kk, lane, R32));
+                if constexpr (SPLIT) vl[p % NL][b][kk] = load_op(v_lo + v_index(w + nw * p, b, kk, lane, R32));
+            }
+
+    // 3. sum the waves' partial projections (the same order in every wave)
+    //    and take P^T as the reprojection's B operand (k-slot e = column 8g + e)
+#pragma unroll
+    for (int jb = 0; jb < NJB; ++jb)
+        *reinterpret_cast<v4f *>(&lp[(w * 16 + tl) * RPS + 16 * jb + 4 * g]) = acc[jb];
+    __syncthreads();
     v8bf ph[R32], pl[R32];
 #pragma unroll
     for (int kk = 0; kk < R32; ++kk) {
-        ph[kk] = load_op(&pbuf[0][tl][32 * kk + 8 * g]);
-        pl[kk] = load_op(&pbuf[1][tl][32 * kk + 8 * g]);
-    }
+        v4f p0 = v4f{0, 0, 0, 0}, p1 = p0;
+        for (int ww = 0; ww < nw; ++ww) {
+            const float *src = &lp[(ww * 16 + tl) * RPS + 32 * kk + 8 * g];
+            p0 += *reinterpret_cast<const v4f *>(src);
+            p1 += *reinterpret_cast<const v4f *>(src + 4);
+        }
+        v4u hi{pk_bf16(p0[0], p0[1]), pk_bf16(p0[2], p0[3]), pk_bf16(p1[0], p1[1]), pk_bf16(p1[2], p1[3])};
+        ph[kk] = as_v8bf(hi);
+        if constexpr (SPLIT) {
+            const float pv[8] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
+            v4u lo;
 #pragma unroll
-    for (int st = 0; st < 2 * CPW; ++st) {
-        const int m = st >> 1, b = st & 1, cur = st & 1;
-        if (st + 1 < 2 * CPW) {
-            const int cn = w + nw * ((st + 1) >> 1), bn = (st + 1) & 1;
+            for (int q = 0; q < 4; ++q) {
+                const float h0 = __uint_as_float(hi[q] << 16), h1 = __uint_as_float(hi[q] & 0xFFFF0000u);
+                lo[q] = pk_bf16(pv[2 * q] - h0, pv[2 * q + 1] - h1);
+            }
+            pl[kk] = as_v8bf(lo);
+        }
+    }
+
+    // 4. reprojection + residual (C: 16 columns of d x 16 tokens, seeded with
+    //    h), rounded to the storage type; with QUANT also the RMSNorm
+    //    statistics of the rounded values
+    double ss = 0.0;
+    float am = 0.0f;
+#pragma unroll
+    for (int m = 0; m < CPW; ++m) {
+        const int sl = m % PD;
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            v4f cacc;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) cacc[v] = hr[m].get(4 * b + v);
 #pragma unroll
             for (int kk = 0; kk < R32; ++kk) {
-                vh[cur ^ 1][kk] = load_op(site + vbase + v_index(cn, bn, kk, 0, lane, R32));
-                vl[cur ^ 1][kk] = load_op(site + vbase + v_index(cn, bn, kk, 1, lane, R32));
+                cacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vh[sl][b][kk], ph[kk], cacc, 0, 0, 0);
+                if constexpr (SPLIT) {
+                    cacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vl[sl % NL][b][kk], ph[kk], cacc, 0, 0, 0);
+                    cacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vh[sl][b][kk], pl[kk], cacc, 0, 0, 0);
+                }
+            }
+            hr[m].set4(b, cacc);
+            if constexpr (QUANT) {
+                // rounding is monotone and odd: the largest rounded magnitude
+                // is the rounded largest magnitude
+#pragma unroll
+                for (int v = 0; v < 4; ++v) am = fmaxf(am, fabsf(cacc[v]));
             }
         }
-        v4f cacc;
+        if constexpr (QUANT) ss += hr[m].sumsq();
+        if (m + PD < CPW) {
+            const int cn = w + nw * (m + PD);
 #pragma unroll
-        for (int v = 0; v < 4; ++v) cacc[v] = hr[m].get(4 * b + v);
+            for (int b = 0; b < 2; ++b)
 #pragma unroll
-        for (int kk = 0; kk < R32; ++kk) {
-            cacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vh[cur][kk], ph[kk], cacc, 0, 0, 0);
-            cacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vl[cur][kk], ph[kk], cacc, 0, 0, 0);
-            cacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vh[cur][kk], pl[kk], cacc, 0, 0, 0);
+                for (int kk = 0; kk < R32; ++kk) {
+                    vh[sl][b][kk] = load_op(v_hi + v_index(cn, b, kk, lane, R32));
+                    if constexpr (SPLIT) vl[sl % NL][b][kk] = load_op(v_lo + v_index(cn, b, kk, lane, R32));
+                }
         }
-#pragma unroll
-        for (int v = 0; v < 4; ++v) hr[m].set(4 * b + v, cacc[v]);
         __builtin_amdgcn_sched_barrier(0);
     }
 
 #pragma unroll
     for (int m = 0; m < CPW; ++m) hr[m].opaque();
     if constexpr (QUANT) {
-        // 5. RMSNorm statistics of the stored (rounded) h'
-        double ss = 0.0;
-        float am = 0.0f;
-#pragma unroll
-        for (int m = 0; m < CPW; ++m) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float x = hr[m].get(e);
-                ss = fma(static_cast<double>(x), static_cast<double>(x), ss);
-                am = fmaxf(am, fabsf(x));
-            }
-            __builtin_amdgcn_sched_barrier(0);
-        }
+        // 5. row statistics over the waves
         ss += shfl_xor_f64(ss, 16);
         ss += shfl_xor_f64(ss, 32);
         am = wave_max_xor(am, 16);
         am = wave_max_xor(am, 32);
-        if (g == 0) { ssq[w][tl] = ss; amx[w][tl] = am; }
+        if (g == 0) {
+            lss[w * 16 + tl] = ss;
+            lam[w * 16 + tl] = am;
+        }
         __syncthreads();
         double tot = 0.0;
         float amax = 0.0f;
-        for (int ww = 0; ww < nw; ++ww) { tot += ssq[ww][tl]; amax = fmaxf(amax, amx[ww][tl]); }
+        for (int ww = 0; ww < nw; ++ww) {
+            tot += lss[ww * 16 + tl];
+            amax = fmaxf(amax, lam[ww * 16 + tl]);
+        }
+        if constexpr (!SPLIT) amax = bf16_to_f32(f32_to_bf16(amax));
         const float inv = static_cast<float>(1.0 / sqrt(tot / static_cast<double>(d) + static_cast<double>(eps)));
         float mval;
         if (norm_w == nullptr) {
@@ -289,18 +341,17 @@ __global__ __launch_bounds__(512) void correct_kernel(
             float a2 = 0.0f;
 #pragma unroll
             for (int m = 0; m < CPW; ++m) {
-                const int c = w + nw * m;
+                const float *wp = norm_w + 32 * (w + nw * m) + 8 * g;
+                const v4f w0 = *reinterpret_cast<const v4f *>(wp), w1 = *reinterpret_cast<const v4f *>(wp + 4);
 #pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    a2 = fmaxf(a2, fabsf((hr[m].get(e) * inv) * norm_w[32 * c + 8 * g + e]));
+                for (int e = 0; e < 8; ++e) a2 = fmaxf(a2, fabsf((hr[m].get(e) * inv) * (e < 4 ? w0[e] : w1[e - 4])));
             }
             a2 = wave_max_xor(a2, 16);
             a2 = wave_max_xor(a2, 32);
-            __syncthreads();
-            if (g == 0) amx[w][tl] = a2;
+            if (g == 0) lwm[w * 16 + tl] = a2;
             __syncthreads();
             mval = 0.0f;
-            for (int ww = 0; ww < nw; ++ww) mval = fmaxf(mval, amx[ww][tl]);
+            for (int ww = 0; ww < nw; ++ww) mval = fmaxf(mval, lwm[ww * 16 + tl]);
         }
 #pragma unroll
         for (int m = 0; m < CPW; ++m) hr[m].opaque();
@@ -311,30 +362,46 @@ __global__ __launch_bounds__(512) void correct_kernel(
         const float inv_s = s > 0.0f ? __fdiv_rn(1.0f, s) : 0.0f;
         const size_t rowb = bits == 4 ? static_cast<size_t>(d) / 2 : static_cast<size_t>(d) * 3 / 8;
 
-        // 6. quantise + pack
-#pragma unroll
-        for (int m = 0; m < CPW; ++m) {
+        // 6. quantise + pack (norm weights, if any, in a loop of their own)
+        auto quant_chunk = [&](int m, const float *wts) {
             const int c = w + nw * m;
-            int q[8];
+            uint32_t u[8];
+            if (wts != nullptr) {
+                const v4f w0 = *reinterpret_cast<const v4f *>(wts + 32 * c + 8 * g);
+                const v4f w1 = *reinterpret_cast<const v4f *>(wts + 32 * c + 8 * g + 4);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                float a = hr[m].get(e) * inv;
-                if (nw_q != nullptr) a *= nw_q[32 * c + 8 * g + e];
-                q[e] = s > 0.0f ? quant_code(a, s, inv_s, qmax) : 0;
+                for (int e = 0; e < 8; ++e) u[e] = quant_bits((hr[m].get(e) * inv) * (e < 4 ? w0[e] : w1[e - 4]), s, inv_s);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) u[e] = quant_bits(hr[m].get(e) * inv, s, inv_s);
             }
             if (bits == 4) {
-                if (valid)
-                    *reinterpret_cast<uint32_t *>(codes + t * rowb + 16 * c + 4 * g) = pack_int4x8(q);
+                uint32_t word = 0;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) word |= (u[e] & 0xFu) << (4 * e);
+                if (valid) *reinterpret_cast<uint32_t *>(codes + t * rowb + 16 * c + 4 * g) = word;
             } else {
-                uint32_t w0, w1, w2;
-                int3_part(q, g, w0, w1, w2);
-                w0 |= __shfl_xor(w0, 16, kWave); w0 |= __shfl_xor(w0, 32, kWave);
-                w1 |= __shfl_xor(w1, 16, kWave); w1 |= __shfl_xor(w1, 32, kWave);
-                w2 |= __shfl_xor(w2, 16, kWave); w2 |= __shfl_xor(w2, 32, kWave);
-                if (valid && g < 3)
-                    *reinterpret_cast<uint32_t *>(codes + t * rowb + 12 * c + 4 * g) = g == 0 ? w0 : (g == 1 ? w1 : w2);
+                uint32_t own, low[3];
+                int3_lane_parts(u, own, low);
+                const int src = 48 + tl;  // the g = 3 lane of this token
+                const uint32_t l0 = __shfl(low[0], src, kWave), l1 = __shfl(low[1], src, kWave),
+                               l2 = __shfl(low[2], src, kWave);
+                const uint32_t word = own | (g == 0 ? l0 : (g == 1 ? l1 : l2));
+                if (valid && g < 3) *reinterpret_cast<uint32_t *>(codes + t * rowb + 12 * c + 4 * g) = word;
             }
-            __builtin_amdgcn_sched_barrier(0);
+        };
+        if (nw_q != nullptr) {
+#pragma unroll
+            for (int m = 0; m < CPW; ++m) {
+                quant_chunk(m, nw_q);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        } else {
+#pragma unroll
+            for (int m = 0; m < CPW; ++m) {
+                quant_chunk(m, nullptr);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
         if (valid && w == 0 && g == 0) scales[t] = s;
     }
@@ -346,13 +413,26 @@ __global__ __launch_bounds__(512) void correct_kernel(
     }
 }
 
+int device_cus() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+    if (dev < 64 && cached[dev] > 0) return cached[dev];
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    if (dev < 64) cached[dev] = cus;
+    return cus;
+}
+
 template <typename T, int CPW, int R32, bool QUANT>
 hipError_t launch_t(const void *h_in, void *h_out, int64_t n, int d, int64_t ld_h, const void *site, int nw,
                     const float *norm_w, float eps, int bits, uint8_t *codes, float *scales, hipStream_t s) {
-    const unsigned blocks = static_cast<unsigned>((n + kTok - 1) / kTok);
+    // 16 tokens per workgroup unless that leaves compute units idle
+    const int tb = (n + 15) / 16 >= device_cus() ? 16 : 8;
+    const unsigned blocks = static_cast<unsigned>((n + tb - 1) / tb);
     hipLaunchKernelGGL((correct_kernel<T, CPW, R32, QUANT>), dim3(blocks), dim3(64 * nw), 0, s,
                        static_cast<const T *>(h_in), static_cast<T *>(h_out), n, d, ld_h,
-                       static_cast<const uint16_t *>(site), nw, norm_w, eps, bits, codes, scales);
+                       static_cast<const uint16_t *>(site), tb, norm_w, eps, bits, codes, scales);
     return hipGetLastError();
 }
 
@@ -373,16 +453,20 @@ hipError_t launch_c(int cpw, int r32, const void *h_in, void *h_out, int64_t n, 
         case 4: return launch_r<T, 4, QUANT>(r32, h_in, h_out, n, d, ld_h, site, nw, norm_w, eps, bits, codes, scales, s);
         case 8: return launch_r<T, 8, QUANT>(r32, h_in, h_out, n, d, ld_h, site, nw, norm_w, eps, bits, codes, scales, s);
         case 16: return launch_r<T, 16, QUANT>(r32, h_in, h_out, n, d, ld_h, site, nw, norm_w, eps, bits, codes, scales, s);
-        default: return launch_r<T, 32, QUANT>(r32, h_in, h_out, n, d, ld_h, site, nw, norm_w, eps, bits, codes, scales, s);
+        default:
+            if constexpr (sizeof(T) == 2)
+                return launch_r<T, 32, QUANT>(r32, h_in, h_out, n, d, ld_h, site, nw, norm_w, eps, bits, codes, scales, s);
+            return hipErrorInvalidValue;
     }
 }
 
 }  // namespace
 
-bool correct_geometry(int64_t d, int *waves, int *chunks_per_wave) {
+bool correct_geometry(int64_t d, bool f32, int *waves, int *chunks_per_wave) {
     if (d <= 0 || d % 32) return false;
     const int64_t nch = d / 32;
     for (int cpw : {1, 2, 4, 8, 16, 32}) {
+        if (f32 && cpw > 16) break;  // a float32 slice of 32 chunks does not fit in registers
         if (nch % cpw == 0 && nch / cpw <= kMaxWaves) {
             *waves = static_cast<int>(nch / cpw);
             *chunks_per_wave = cpw;
@@ -405,7 +489,7 @@ hipError_t launch_correct(const void *h_in, void *h_out, int h_dtype, int64_t n,
                           const void *site, int r, bool quant, const float *norm_w, float eps, int bits,
                           uint8_t *codes, float *scales, hipStream_t s) {
     int nw = 0, cpw = 0;
-    if (!correct_geometry(d, &nw, &cpw)) return hipErrorInvalidValue;
+    if (!correct_geometry(d, h_dtype == 0, &nw, &cpw)) return hipErrorInvalidValue;
     const int r32 = rank_pad(r) / 32;
     if (h_dtype == 1) {
         if (quant) return launch_c<uint16_t, true>(cpw, r32, h_in, h_out, n, d, ld_h, site, nw, norm_w, eps, bits, codes, scales, s);

@@ -32,6 +32,24 @@ __device__ __forceinline__ void split_bf16(float f, uint16_t &hi, uint16_t &lo) 
     lo = f32_to_bf16(f - bf16_to_f32(hi));
 }
 
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+
+// Two floats -> two bfloat16 (nearest even) in one word, low half first
+// (one v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
+    v2bf p;
+    p[0] = static_cast<__bf16>(a);
+    p[1] = static_cast<__bf16>(b);
+    uint32_t u;
+    __builtin_memcpy(&u, &p, 4);
+    return u;
+}
+__device__ __forceinline__ v2bf as_v2bf(uint32_t u) {
+    v2bf p;
+    __builtin_memcpy(&p, &u, 4);
+    return p;
+}
+
 __device__ __forceinline__ v8bf as_v8bf(v4u x) {
     v8bf r;
     __builtin_memcpy(&r, &x, 16);
@@ -63,6 +81,40 @@ __device__ __forceinline__ int quant_code(float a, float s, float inv_s, int qma
     }
     q = fminf(fmaxf(q, -static_cast<float>(qmax)), static_cast<float>(qmax));
     return static_cast<int>(q);
+}
+
+// Code of a / s, for |a| <= qmax * s: the float32 quotient rounded to nearest,
+// then to the nearest integer (ties to even), as in rint(a / s). The quotient
+// starts as RN(a * inv_s) (inv_s = RN(1 / s)), within one ulp of a / s; one
+// residual step r = a - y0 s (exact in an fma), y = RN(y0 + r inv_s) then
+// gives RN(a / s) exactly (Markstein's theorem on fma-based division, IBM J.
+// Res. Dev. 34(1), 1990). Adding 1.5 * 2^23 rounds y to an integer, ties to
+// even, and leaves that integer in the low mantissa bits: the returned word's
+// low 4 (or 3) bits are the two's complement code. s = 0 (inv_s = 0) gives 0.
+__device__ __forceinline__ uint32_t quant_bits(float a, float s, float inv_s) {
+    const float y0 = a * inv_s;
+    const float r = fmaf(-y0, s, a);
+    const float y = fmaf(r, inv_s, y0);
+    return __float_as_uint(y + 12582912.0f);
+}
+
+// int3 packing without lane-dependent control flow. Lane group g (0..3) of a
+// 32-code group holds codes 8g .. 8g+7 (code bits in the low 3 bits of u[e]),
+// i.e. slots 2g (e < 4) and 2g + 1 (e >= 4), byte lane e % 4. Slots 2g and
+// 2g+1 of g < 3 fill bits 5-7 and 2-4 of word g alone; slots 6 and 7 (g = 3)
+// fill bits 0-1 of words 0 and 1 and bits 1 and 0 of word 2. own: this lane's
+// contribution if g < 3; low[i]: its contribution to word i if g = 3.
+__device__ __forceinline__ void int3_lane_parts(const uint32_t u[8], uint32_t &own, uint32_t low[3]) {
+    own = 0;
+    low[0] = low[1] = low[2] = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        const uint32_t lo = u[b] & 7u, hi = u[4 + b] & 7u;
+        own |= (lo << (8 * b + 5)) | (hi << (8 * b + 2));
+        low[0] |= (lo & 3u) << (8 * b);
+        low[1] |= (hi & 3u) << (8 * b);
+        low[2] |= ((lo >> 2) << (8 * b + 1)) | ((hi >> 2) << (8 * b));
+    }
 }
 
 // Pack 8 int4 codes (code e at nibble e) into one 32-bit word: byte j = c[2j] | c[2j+1] << 4.

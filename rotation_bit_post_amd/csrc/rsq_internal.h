@@ -9,12 +9,14 @@ namespace rsq {
 // r rounded up to a multiple of 32 (the matrix-core K step of the reprojection).
 inline int rank_pad(int r) { return (r + 31) / 32 * 32; }
 
-// Bytes of a prepared site: U and V = U M^T, each as bf16 hi + lo, d x r_pad.
+// Bytes of a prepared site: U and V = U M^T, each as bf16 hi + lo, d x r_pad
+// (parts U hi, V hi, U lo, V lo).
 inline size_t site_bytes(int64_t d, int r) { return static_cast<size_t>(d) * rank_pad(r) * 2 * 2 * 2; }
 
 // Waves per workgroup and 32-column chunks per wave of the correction kernel
-// for width d; returns false if d cannot be split evenly.
-bool correct_geometry(int64_t d, int *waves, int *chunks_per_wave);
+// for width d (f32: float32 residual, at most 16 chunks per wave); returns
+// false if d cannot be split evenly.
+bool correct_geometry(int64_t d, bool f32, int *waves, int *chunks_per_wave);
 
 hipError_t launch_site_prepare(const float *U, const float *M, int d, int r, void *site, hipStream_t s);
 

@@ -34,9 +34,10 @@ def run_site(h_dev, U, M, bits, dtype):
     import torch
     rsq = lib()
     n, d = h_dev.shape
+    r = U.shape[1]
     out = torch.empty_like(h_dev)
     codes, scales = empty_u8(n, rsq.rsq_packed_row_bytes(d, bits)), empty_f32(n)
-    rsq.rsq_correct_quant(h_dev, out, gpu_site(U, M), U.shape[1], codes, scales, bits)
+    rsq.rsq_correct_quant(h_dev, out, gpu_site(U, M), r, codes, scales, bits)
     torch.cuda.synchronize()
     return out, codes, scales
 
@@ -117,11 +118,11 @@ def test_config1_tiny_block_end_to_end():
     if np.array_equal(q_gpu, ref["q"]):
         assert rel_l2(to_host(y), ref["y"]) < 1e-6
     # the device weight quantiser reproduces the oracle's weight codes
-    wc, ws = empty_u8(N, cfg.D // 2), empty_f32(N)
-    rsq.rsq_quant_act(to_dev(w, "f32"), wc, ws, cfg.bits)
+    wc, wsc = empty_u8(N, cfg.D // 2), empty_f32(N)
+    rsq.rsq_quant_act(to_dev(w, "f32"), wc, wsc, cfg.bits)
     torch.cuda.synchronize()
     assert code_mismatch_ok(packing.unpack(wc.cpu().numpy(), cfg.D, cfg.bits), qw)[0]
-    assert np.all(np.abs(ws.cpu().numpy() - sw) <= 1e-6 * sw)
+    assert np.all(np.abs(wsc.cpu().numpy() - sw) <= 1e-6 * sw)
 
 
 # ------------------------------------------------------------- configs 2, 3
@@ -149,13 +150,13 @@ def test_config2_weight_quantisation_on_device():
     rsq = lib()
     cfg = synth.CONFIGS[2]
     w = np.concatenate([synth.weight(cfg, p, cfg.D, cfg.D) for p in ("q", "k", "v")], axis=0)
-    wc, ws = empty_u8(w.shape[0], cfg.D // 2), empty_f32(w.shape[0])
-    rsq.rsq_quant_act(to_dev(w, "f32"), wc, ws, cfg.bits)
+    wc, wsc = empty_u8(w.shape[0], cfg.D // 2), empty_f32(w.shape[0])
+    rsq.rsq_quant_act(to_dev(w, "f32"), wc, wsc, cfg.bits)
     torch.cuda.synchronize()
     qw, sw = prep.quantize_weight(w, cfg.bits)
     ok, nbad, _ = code_mismatch_ok(packing.unpack(wc.cpu().numpy(), cfg.D, cfg.bits), qw)
     assert ok, nbad
-    assert np.all(np.abs(ws.cpu().numpy() - sw) <= 1e-6 * sw)
+    assert np.all(np.abs(wsc.cpu().numpy() - sw) <= 1e-6 * sw)
 
 
 @pytest.mark.parametrize("n", [1, 8, 64])

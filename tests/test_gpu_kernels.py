@@ -172,7 +172,12 @@ def test_fused_correct_quant_equals_unfused_and_oracle():
         rsq.rsq_subspace_correct(hd, h2, site, r)
         rsq.rsq_quant_act(h2, c2, s2, bits, rmsnorm=True)
         torch.cuda.synchronize()
-        assert torch.equal(h1, h2) and torch.equal(c1, c2) and torch.equal(s1, s2)
+        # h' bit-identical; the statistics differ only in summation order
+        assert torch.equal(h1, h2)
+        s1h, s2h = s1.cpu().numpy(), s2.cpu().numpy()
+        assert np.all(np.abs(s1h - s2h) <= 4e-7 * s2h)
+        ok, nbad, _ = code_mismatch_ok(packing.unpack(c1.cpu().numpy(), d, bits), packing.unpack(c2.cpu().numpy(), d, bits))
+        assert ok, nbad
         # against the oracle: h' within tolerance, codes from the oracle quantiser on the GPU's h'
         assert rel_l2(to_host(h1), online.correct(h, U, M, dtype)) <= (1e-3 if dtype == "f32" else 2e-2)
         q_ref, s_ref = online.quant_act(to_host(h1), bits, True, 1e-5)
@@ -266,3 +271,29 @@ def test_layer_fused_matches_oracle():
     y_ref = online.dequant(online.gemm(q_gpu, qw), s_gpu, sw, "f32")
     assert np.array_equal(to_host(y), y_ref)
     assert rel_l2(to_host(y), ref["y"]) < 1e-2
+
+
+def test_many_blocks_norm_weight_and_determinism():
+    """Several waves of workgroups over the chip, a ragged last block, a norm weight, repeat runs."""
+    rsq = lib()
+    import torch
+    d, r, bits = 8192, 32, 4
+    n = 16 * 256 * 3 + 37            # more token blocks than compute units, ragged tail
+    U, M = random_site(d, r, seed=31, eps=0.02)
+    site = gpu_site(U, M)
+    h = residual(n, d, "bf16", seed=32)
+    w = np.random.default_rng(33).uniform(0.5, 1.5, d).astype(np.float32)
+    hd = to_dev(h, "bf16")
+    outs = []
+    for _ in range(2):
+        h1, c1, s1 = torch.empty_like(hd), empty_u8(n, d // 2), empty_f32(n)
+        rsq.rsq_correct_quant(hd, h1, site, r, c1, s1, bits, norm_w=to_dev(w, "f32"))
+        outs.append((h1, c1, s1))
+    torch.cuda.synchronize()
+    assert all(torch.equal(a, b) for a, b in zip(outs[0], outs[1]))
+    h1, c1, s1 = outs[0]
+    assert rel_l2(to_host(h1), online.correct(h, U, M, "bf16")) < 2e-2
+    q_ref, s_ref = online.quant_act(to_host(h1), bits, True, 1e-5, w)
+    assert code_mismatch_ok(packing.unpack(c1.cpu().numpy(), d, bits), q_ref)[0]
+    assert np.all(np.abs(s1.cpu().numpy() - s_ref) <= 1e-6 * s_ref)
+
