@@ -41,7 +41,26 @@ def parse():
     p.add_argument("--copies", type=int, default=2)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample", type=int, default=16, help="tokens in the CPU oracle sample")
+    p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                   help="only run a plain device copy of MIB MiB (calibrates rocprofv3 byte counters) and exit")
     return p.parse_args()
+
+
+def progress(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def copy_probe(mib: int) -> None:
+    """A plain device-to-device copy of known size: under rocprofv3 --pmc its
+    FETCH_SIZE / WRITE_SIZE per dispatch give the counters' scale factor."""
+    import torch
+    nbytes = mib << 20
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_read": nbytes, "copy_probe_bytes_written": nbytes, "dispatches": 3}))
 
 
 def kernel_source_hash() -> str:
@@ -98,14 +117,19 @@ def main():
                           "n_gpus": args.gpus}))
         sys.exit(2)
     import torch
+    torch.cuda.set_device(0)
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
     from rotation_bit_post_amd.path import LayerPath
 
-    torch.cuda.set_device(0)
     t_build = time.perf_counter()
+    progress(f"building config {args.config} (sites, weights, inputs)")
     base = LayerPath.build(args.config)
     copies = [base] + [base.clone() for _ in range(args.copies - 1)]
     torch.cuda.synchronize()
     t_build = time.perf_counter() - t_build
+    progress(f"built in {t_build:.1f} s; warm-up {args.warmup}, timing {args.steps} steps")
     cfg, n = base.cfg, base.n
     stage_lists = [p.stages(correction=True) for p in copies]
     names = [s[0] for s in stage_lists[0]]
@@ -133,6 +157,7 @@ def main():
     stage_ms = {nm: [ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(args.steps)] for j, nm in enumerate(names)}
     ms_per_step = sum(step_ms) / len(step_ms)
 
+    progress("timed region done; correction-off pass")
     # correction off: each site only normalises and quantises (one global rotation, T = I)
     off_lists = [p.stages(correction=False) for p in copies]
     for i in range(args.warmup):
@@ -208,6 +233,7 @@ def main():
         "kernel_source_hash": src_hash,
     }
     if not args.no_cpu_baseline:
+        progress(f"CPU oracle on a {args.cpu_sample}-token sample")
         out["cpu_baseline"] = cpu_baseline(base, args.cpu_sample)
     print(json.dumps(out), flush=True)
 

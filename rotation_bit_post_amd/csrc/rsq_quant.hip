@@ -1,12 +1,12 @@
 // Per-token symmetric activation quantisation with optional RMSNorm.
 //
-// One 256-thread workgroup per row: thread t owns 8-element chunks
-// t, t + 256, ... of the row and keeps them in registers across the three
-// steps (statistics, scale, quantise + pack), so the row is read from HBM
-// once. Statistics reduce in a fixed order (lane tree, then waves), so the
-// result does not depend on scheduling. Chunks 4i..4i+3 (one 32-code group)
-// sit in 4 neighbouring lanes, which lets the int3 words be assembled with
-// two lane exchanges.
+// WPR waves (1, 2 or 4) own one row and keep it in registers across the
+// three steps (statistics, scale, quantise + pack), so the row is read from
+// HBM once; a 256-thread workgroup holds 4 / WPR rows. Lane l of wave s of a
+// row owns the 8-element chunks s*64 + l + 64*WPR*m, so a wave's loads are
+// contiguous. Statistics reduce in a fixed order (lane tree, then the row's
+// waves through LDS), so the result does not depend on scheduling. The four
+// chunks of a 32-code int3 group sit in four neighbouring lanes.
 #include "rsq_device.h"
 #include "rsq_internal.h"
 
@@ -25,6 +25,15 @@ template <> struct Chunk8<uint16_t> {
         const uint32_t w = raw[e >> 1];
         return __uint_as_float((e & 1) ? (w & 0xFFFF0000u) : (w << 16));
     }
+    // squares of bf16 values are exact in float32; 8 of them are added in
+    // float32, the chunks in float64
+    __device__ __forceinline__ double sumsq() const {
+        float s = 0.0f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) s = __builtin_amdgcn_fdot2_f32_bf16(as_v2bf(raw[q]), as_v2bf(raw[q]), s, false);
+        return static_cast<double>(s);
+    }
+    __device__ __forceinline__ void opaque() { asm volatile("" : "+v"(raw)); }
 };
 template <> struct Chunk8<float> {
     v4f a, b;
@@ -34,130 +43,173 @@ template <> struct Chunk8<float> {
     }
     __device__ __forceinline__ void zero() { a = v4f{0, 0, 0, 0}; b = a; }
     __device__ __forceinline__ float get(int e) const { return e < 4 ? a[e] : b[e - 4]; }
+    __device__ __forceinline__ double sumsq() const {  // float64 products and adds
+        double s = 0.0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s = fma(static_cast<double>(get(e)), static_cast<double>(get(e)), s);
+        return s;
+    }
+    __device__ __forceinline__ void opaque() { asm volatile("" : "+v"(a), "+v"(b)); }
 };
 
-// CH: maximum chunks per thread (compile time); the row has k / 8 chunks.
-template <typename T, int CH>
+// CH: chunks per lane (compile time); WPR: waves per row.
+template <typename T, int CH, int WPR>
 __global__ __launch_bounds__(kThreads) void quant_kernel(const T *__restrict__ x, int64_t n, int k, int64_t ld_x,
                                                         int norm, const float *__restrict__ norm_w, float eps,
                                                         int bits, uint8_t *__restrict__ codes,
                                                         float *__restrict__ scales) {
-    __shared__ double ssq[kThreads / kWave];
-    __shared__ float amx[kThreads / kWave];
-    const int64_t row = blockIdx.x;
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    constexpr int RPB = 4 / WPR;  // rows per workgroup
+    __shared__ double lss[4];
+    __shared__ float lam[4], lwm[4];
+    const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+    const int lane = threadIdx.x & 63;
+    const int rw = w / WPR, sub = w % WPR;
+    const int64_t row = static_cast<int64_t>(blockIdx.x) * RPB + rw;
+    const bool rvalid = row < n;
     const int nch = k / 8;
-    const T *xr = x + row * ld_x;
+    const T *xr = x + (rvalid ? row : n - 1) * ld_x;
+    auto chunk = [&](int m) { return sub * 64 + lane + 64 * WPR * m; };
 
     Chunk8<T> v[CH];
 #pragma unroll
     for (int m = 0; m < CH; ++m) {
-        const int c = tid + kThreads * m;
-        if (c < nch) v[m].load(xr + 8 * c);
+        if (chunk(m) < nch) v[m].load(xr + 8 * chunk(m));
         else v[m].zero();
     }
 
-    // statistics: sum of squares (float64) and max |x|
+    // statistics: sum of squares and max |x|
     double ss = 0.0;
     float am = 0.0f;
 #pragma unroll
-    for (int m = 0; m < CH; ++m)
+    for (int m = 0; m < CH; ++m) {
+        if (norm) ss += v[m].sumsq();
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float xv = v[m].get(e);
-            ss = fma(static_cast<double>(xv), static_cast<double>(xv), ss);
-            am = fmaxf(am, fabsf(xv));
-        }
+        for (int e = 0; e < 8; ++e) am = fmaxf(am, fabsf(v[m].get(e)));
+    }
 #pragma unroll
     for (int off = 1; off < kWave; off <<= 1) {
         ss += shfl_xor_f64(ss, off);
         am = wave_max_xor(am, off);
     }
-    if (lane == 0) { ssq[wv] = ss; amx[wv] = am; }
-    __syncthreads();
-    double tot = 0.0;
-    float amax = 0.0f;
+    if constexpr (WPR > 1) {
+        if (lane == 0) { lss[w] = ss; lam[w] = am; }
+        __syncthreads();
+        ss = 0.0;
+        am = 0.0f;
 #pragma unroll
-    for (int i = 0; i < kThreads / kWave; ++i) { tot += ssq[i]; amax = fmaxf(amax, amx[i]); }
+        for (int i = 0; i < WPR; ++i) { ss += lss[rw * WPR + i]; am = fmaxf(am, lam[rw * WPR + i]); }
+    }
 
     float inv = 1.0f;
-    float mval = amax;
+    float mval = am;
     if (norm) {
-        inv = static_cast<float>(1.0 / sqrt(tot / static_cast<double>(k) + static_cast<double>(eps)));
+        inv = static_cast<float>(1.0 / sqrt(ss / static_cast<double>(k) + static_cast<double>(eps)));
         if (norm_w == nullptr) {
-            mval = amax * inv;  // rounding is monotone: max|x * inv| = max|x| * inv
+            mval = am * inv;  // rounding is monotone: max|x * inv| = max|x| * inv
         } else {
             float a2 = 0.0f;
 #pragma unroll
             for (int m = 0; m < CH; ++m) {
-                const int c = tid + kThreads * m;
+                const int c = chunk(m);
                 if (c < nch)
 #pragma unroll
                     for (int e = 0; e < 8; ++e) a2 = fmaxf(a2, fabsf((v[m].get(e) * inv) * norm_w[8 * c + e]));
             }
 #pragma unroll
             for (int off = 1; off < kWave; off <<= 1) a2 = wave_max_xor(a2, off);
-            __syncthreads();
-            if (lane == 0) amx[wv] = a2;
-            __syncthreads();
-            mval = 0.0f;
+            if constexpr (WPR > 1) {
+                if (lane == 0) lwm[w] = a2;
+                __syncthreads();
+                a2 = 0.0f;
 #pragma unroll
-            for (int i = 0; i < kThreads / kWave; ++i) mval = fmaxf(mval, amx[i]);
+                for (int i = 0; i < WPR; ++i) a2 = fmaxf(a2, lwm[rw * WPR + i]);
+            }
+            mval = a2;
         }
     }
+#pragma unroll
+    for (int m = 0; m < CH; ++m) v[m].opaque();
     const int qmax = (1 << (bits - 1)) - 1;
     const float s = __fdiv_rn(mval, static_cast<float>(qmax));
     const float inv_s = s > 0.0f ? __fdiv_rn(1.0f, s) : 0.0f;
     const size_t rowb = bits == 4 ? static_cast<size_t>(k) / 2 : static_cast<size_t>(k) * 3 / 8;
-    uint8_t *cr = codes + row * rowb;
+    uint8_t *cr = codes + (rvalid ? row : 0) * rowb;
 
+    // quantise + pack; a = x (no norm), x * inv, or (x * inv) * w
+    auto quant_chunk = [&](int m, bool nrm, const float *wts) {
+        const int c = chunk(m);
+        uint32_t u[8];
+        if (wts != nullptr) {
+            const int cc = c < nch ? c : nch - 1;
+            const v4f w0 = *reinterpret_cast<const v4f *>(wts + 8 * cc);
+            const v4f w1 = *reinterpret_cast<const v4f *>(wts + 8 * cc + 4);
 #pragma unroll
-    for (int m = 0; m < CH; ++m) {
-        const int c = tid + kThreads * m;
-        int q[8];
+            for (int e = 0; e < 8; ++e) u[e] = quant_bits((v[m].get(e) * inv) * (e < 4 ? w0[e] : w1[e - 4]), s, inv_s);
+        } else if (nrm) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            float a = v[m].get(e);
-            if (norm) {
-                a *= inv;
-                if (norm_w != nullptr && c < nch) a *= norm_w[8 * c + e];
-            }
-            q[e] = s > 0.0f ? quant_code(a, s, inv_s, qmax) : 0;
+            for (int e = 0; e < 8; ++e) u[e] = quant_bits(v[m].get(e) * inv, s, inv_s);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) u[e] = quant_bits(v[m].get(e), s, inv_s);
         }
         if (bits == 4) {
-            if (c < nch) *reinterpret_cast<uint32_t *>(cr + 4 * c) = pack_int4x8(q);
-        } else if (kThreads * m < nch) {  // whole 32-code groups are in or out together
-            uint32_t w0, w1, w2;
-            const int qpos = c & 3;
-            int3_part(q, qpos, w0, w1, w2);
-            w0 |= __shfl_xor(w0, 1, kWave); w0 |= __shfl_xor(w0, 2, kWave);
-            w1 |= __shfl_xor(w1, 1, kWave); w1 |= __shfl_xor(w1, 2, kWave);
-            w2 |= __shfl_xor(w2, 1, kWave); w2 |= __shfl_xor(w2, 2, kWave);
-            if (c < nch && qpos < 3)
-                *reinterpret_cast<uint32_t *>(cr + 12 * (c >> 2) + 4 * qpos) = qpos == 0 ? w0 : (qpos == 1 ? w1 : w2);
+            uint32_t word = 0;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) word |= (u[e] & 0xFu) << (4 * e);
+            if (rvalid && c < nch) *reinterpret_cast<uint32_t *>(cr + 4 * c) = word;
+        } else {
+            uint32_t own, low[3];
+            int3_lane_parts(u, own, low);
+            const int src = lane | 3;  // the lane holding slots 6 and 7 of this group
+            const uint32_t l0 = __shfl(low[0], src, kWave), l1 = __shfl(low[1], src, kWave),
+                           l2 = __shfl(low[2], src, kWave);
+            const int q = lane & 3;
+            const uint32_t word = own | (q == 0 ? l0 : (q == 1 ? l1 : l2));
+            if (rvalid && c < nch && q < 3) *reinterpret_cast<uint32_t *>(cr + 12 * (c >> 2) + 4 * q) = word;
         }
+    };
+    if (norm && norm_w != nullptr) {
+#pragma unroll
+        for (int m = 0; m < CH; ++m) quant_chunk(m, true, norm_w);
+    } else if (norm) {
+#pragma unroll
+        for (int m = 0; m < CH; ++m) quant_chunk(m, true, nullptr);
+    } else {
+#pragma unroll
+        for (int m = 0; m < CH; ++m) quant_chunk(m, false, nullptr);
     }
-    if (tid == 0) scales[row] = s;
+    if (rvalid && sub == 0 && lane == 0) scales[row] = s;
 }
 
-template <typename T, int CH>
+template <typename T, int CH, int WPR>
 hipError_t launch_t(const void *x, int64_t n, int k, int64_t ld_x, bool norm, const float *norm_w, float eps,
                     int bits, uint8_t *codes, float *scales, hipStream_t s) {
-    hipLaunchKernelGGL((quant_kernel<T, CH>), dim3(static_cast<unsigned>(n)), dim3(kThreads), 0, s,
-                       static_cast<const T *>(x), n, k, ld_x, norm ? 1 : 0, norm_w, eps, bits, codes, scales);
+    constexpr int RPB = 4 / WPR;
+    hipLaunchKernelGGL((quant_kernel<T, CH, WPR>), dim3(static_cast<unsigned>((n + RPB - 1) / RPB)), dim3(kThreads),
+                       0, s, static_cast<const T *>(x), n, k, ld_x, norm ? 1 : 0, norm_w, eps, bits, codes, scales);
     return hipGetLastError();
 }
 
-template <typename T>
-hipError_t launch_ch(const void *x, int64_t n, int k, int64_t ld_x, bool norm, const float *norm_w, float eps,
-                     int bits, uint8_t *codes, float *scales, hipStream_t s) {
-    const int need = (k / 8 + kThreads - 1) / kThreads;
-    if (need <= 1) return launch_t<T, 1>(x, n, k, ld_x, norm, norm_w, eps, bits, codes, scales, s);
-    if (need <= 2) return launch_t<T, 2>(x, n, k, ld_x, norm, norm_w, eps, bits, codes, scales, s);
-    if (need <= 4) return launch_t<T, 4>(x, n, k, ld_x, norm, norm_w, eps, bits, codes, scales, s);
-    if (need <= 8) return launch_t<T, 8>(x, n, k, ld_x, norm, norm_w, eps, bits, codes, scales, s);
-    if (need <= 16) return launch_t<T, 16>(x, n, k, ld_x, norm, norm_w, eps, bits, codes, scales, s);
+template <typename T, int WPR>
+hipError_t launch_ch(int nch, const void *x, int64_t n, int k, int64_t ld_x, bool norm, const float *norm_w,
+                     float eps, int bits, uint8_t *codes, float *scales, hipStream_t s) {
+    const int need = (nch + 64 * WPR - 1) / (64 * WPR);
+    if (need <= 1) return launch_t<T, 1, WPR>(x, n, k, ld_x, norm, norm_w, eps, bits, codes, scales, s);
+    if (need <= 2) return launch_t<T, 2, WPR>(x, n, k, ld_x, norm, norm_w, eps, bits, codes, scales, s);
+    if (need <= 4) return launch_t<T, 4, WPR>(x, n, k, ld_x, norm, norm_w, eps, bits, codes, scales, s);
+    if (need <= 8) return launch_t<T, 8, WPR>(x, n, k, ld_x, norm, norm_w, eps, bits, codes, scales, s);
+    if (need <= 16) return launch_t<T, 16, WPR>(x, n, k, ld_x, norm, norm_w, eps, bits, codes, scales, s);
     return hipErrorInvalidValue;
+}
+
+// One wave per row up to 4096 elements, then two, then four waves.
+template <typename T>
+hipError_t launch_w(const void *x, int64_t n, int k, int64_t ld_x, bool norm, const float *norm_w, float eps,
+                    int bits, uint8_t *codes, float *scales, hipStream_t s) {
+    const int nch = k / 8;
+    if (nch <= 64 * 8) return launch_ch<T, 1>(nch, x, n, k, ld_x, norm, norm_w, eps, bits, codes, scales, s);
+    if (nch <= 128 * 8) return launch_ch<T, 2>(nch, x, n, k, ld_x, norm, norm_w, eps, bits, codes, scales, s);
+    return launch_ch<T, 4>(nch, x, n, k, ld_x, norm, norm_w, eps, bits, codes, scales, s);
 }
 
 }  // namespace
@@ -165,8 +217,8 @@ hipError_t launch_ch(const void *x, int64_t n, int k, int64_t ld_x, bool norm, c
 hipError_t launch_quant(const void *x, int x_dtype, int64_t n, int k, int64_t ld_x, bool norm,
                         const float *norm_w, float eps, int bits, uint8_t *codes, float *scales,
                         hipStream_t s) {
-    if (x_dtype == 1) return launch_ch<uint16_t>(x, n, k, ld_x, norm, norm_w, eps, bits, codes, scales, s);
-    return launch_ch<float>(x, n, k, ld_x, norm, norm_w, eps, bits, codes, scales, s);
+    if (x_dtype == 1) return launch_w<uint16_t>(x, n, k, ld_x, norm, norm_w, eps, bits, codes, scales, s);
+    return launch_w<float>(x, n, k, ld_x, norm, norm_w, eps, bits, codes, scales, s);
 }
 
 }  // namespace rsq
