@@ -413,17 +413,6 @@ __global__ __launch_bounds__(64 * kMaxWaves) void correct_kernel(
     }
 }
 
-int device_cus() {
-    static int cached[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
-    if (dev < 64 && cached[dev] > 0) return cached[dev];
-    int cus = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-    if (dev < 64) cached[dev] = cus;
-    return cus;
-}
-
 template <typename T, int CPW, int R32, bool QUANT>
 hipError_t launch_t(const void *h_in, void *h_out, int64_t n, int d, int64_t ld_h, const void *site, int nw,
                     const float *norm_w, float eps, int bits, uint8_t *codes, float *scales, hipStream_t s) {
@@ -461,6 +450,17 @@ hipError_t launch_c(int cpw, int r32, const void *h_in, void *h_out, int64_t n, 
 }
 
 }  // namespace
+
+int device_cus() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+    if (dev < 64 && cached[dev] > 0) return cached[dev];
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    if (dev < 64) cached[dev] = cus;
+    return cus;
+}
 
 bool correct_geometry(int64_t d, bool f32, int *waves, int *chunks_per_wave) {
     if (d <= 0 || d % 32) return false;

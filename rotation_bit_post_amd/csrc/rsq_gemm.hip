@@ -37,7 +37,9 @@ template <> struct Fmt<3> {
 
 template <typename YT> __device__ __forceinline__ YT to_out(float v);
 template <> __device__ __forceinline__ float to_out<float>(float v) { return v; }
-template <> __device__ __forceinline__ uint16_t to_out<uint16_t>(float v) { return f32_to_bf16(v); }
+template <> __device__ __forceinline__ uint16_t to_out<uint16_t>(float v) {
+    return static_cast<uint16_t>(pk_bf16(v, 0.0f));  // nearest even, one instruction
+}
 
 // One group of 32 packed codes, as loaded from HBM.
 template <int BITS> struct Group;
@@ -247,6 +249,38 @@ __global__ __launch_bounds__(WM * WN * 64) void qgemm_kernel(const uint8_t *__re
         T::template run<false>(lds, A, W, n, N, K, bm0, bn0, acc);
 
     // epilogue: lane holds channel l32 of each fragment and tokens 8(v/4) + 4h + v%4
+    constexpr int OS = BN + 8;  // bf16 row stride of the output tile in LDS
+    const bool staged = sizeof(YT) == 2 && acc_out == nullptr && ld_y % 8 == 0 &&
+                        (reinterpret_cast<uintptr_t>(y) & 15) == 0 && BM * OS * 2 <= T::LDS_BYTES;
+    if (staged) {
+        // bf16 tile through LDS, then 16-byte row-contiguous stores
+        uint16_t *ot = reinterpret_cast<uint16_t *>(lds);
+        __syncthreads();  // every wave is done with the operand tiles
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int cl = wn * (BN / WN) + 32 * j + l32;
+            const float swj = bn0 + cl < N ? sw[bn0 + cl] : 0.0f;
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int tl = wm * (BM / WM) + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
+                    const float sat = bm0 + tl < n ? sa[bm0 + tl] : 0.0f;
+                    const float val = (static_cast<float>(acc[i][j][v] >> F::kShift) * sat) * swj;
+                    ot[tl * OS + cl] = to_out<uint16_t>(val);
+                }
+            }
+        }
+        __syncthreads();
+        constexpr int CPR = BN / 8;  // 16-byte chunks per row
+        for (int c = threadIdx.x; c < BM * CPR; c += WM * WN * 64) {
+            const int r = c / CPR, q = c % CPR;
+            if (bm0 + r < n && bn0 + 8 * q < N)
+                *reinterpret_cast<v4u *>(y + static_cast<int64_t>(bm0 + r) * ld_y + bn0 + 8 * q) =
+                    *reinterpret_cast<const v4u *>(ot + r * OS + 8 * q);
+        }
+        return;
+    }
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
         const int ch = bn0 + wn * (BN / WN) + 32 * j + l32;
@@ -278,16 +312,24 @@ hipError_t launch_t(const uint8_t *a, const float *sa, int64_t n, const uint8_t 
     return hipGetLastError();
 }
 
-// Tile shape by problem size (measured on MI355X: 256 x 128 tiles with 8
-// waves lead on the layer shapes; smaller tiles keep small batches spread
-// over the CUs).
+// Tile shape by problem size (measured on MI355X): 256 x 128 tiles with 8
+// waves on the layer shapes, 256 x 256 when the smaller tile would need
+// clearly more rounds of workgroups over the compute units (a 256 x 256 tile
+// does twice the work at about 10 % better efficiency); smaller tiles keep
+// small batches spread over the CUs.
 template <int BITS, typename YT>
 hipError_t launch_b(const uint8_t *a, const float *sa, int64_t n, const uint8_t *w, const float *sw, int64_t N,
                     int64_t K, void *y, int64_t ld_y, int32_t *acc_out, hipStream_t s) {
     if (n <= 32) return launch_t<BITS, 32, 128, 1, 4, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, s);
     if (n <= 64) return launch_t<BITS, 64, 128, 2, 2, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, s);
-    const int64_t tiles = ((n + 255) / 256) * ((N + 127) / 128);
-    if (n >= 256 && tiles >= 200) return launch_t<BITS, 256, 128, 4, 2, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, s);
+    const int64_t cus = device_cus();
+    const int64_t mt = (n + 255) / 256;
+    const int64_t rounds_128 = (mt * ((N + 127) / 128) + cus - 1) / cus;
+    const int64_t rounds_256 = (mt * ((N + 255) / 256) + cus - 1) / cus;
+    if (n >= 256 && 18 * rounds_256 < 10 * rounds_128)
+        return launch_t<BITS, 256, 256, 4, 2, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, s);
+    if (n >= 256 && mt * ((N + 127) / 128) >= 200)
+        return launch_t<BITS, 256, 128, 4, 2, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, s);
     return launch_t<BITS, 128, 128, 2, 2, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, s);
 }
 

@@ -18,6 +18,9 @@ inline size_t site_bytes(int64_t d, int r) { return static_cast<size_t>(d) * ran
 // false if d cannot be split evenly.
 bool correct_geometry(int64_t d, bool f32, int *waves, int *chunks_per_wave);
 
+// Compute units of the current device (cached per device).
+int device_cus();
+
 hipError_t launch_site_prepare(const float *U, const float *M, int d, int r, void *site, hipStream_t s);
 
 // h_dtype: 0 float32, 1 bfloat16. quant: also RMSNorm + quantise + pack.

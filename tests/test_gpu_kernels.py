@@ -227,6 +227,38 @@ def test_qgemm_bit_exact(bits, n, N, K, ydt):
     assert torch.equal(y, y2)
 
 
+@pytest.mark.parametrize("bits,n,N,K", [(4, 1000, 12320, 4096), (4, 2000, 22048, 1056), (3, 2000, 22048, 4096)])
+def test_qgemm_large_tiles_with_ragged_edges(bits, n, N, K):
+    """Shapes that take the 256 x 256 tiles, with partial tiles in tokens, channels and k.
+
+    The y-only launch (LDS-staged epilogue) must equal the launch that also
+    writes the accumulators (direct epilogue); sampled blocks match the oracle.
+    """
+    rsq = lib()
+    import torch
+    print(f"case qgemm-large bits={bits} n={n} N={N} K={K}", flush=True)
+    rng = np.random.default_rng(n + N + K + bits)
+    qa, qw = _random_codes(n, K, bits, rng), _random_codes(N, K, bits, rng)
+    sa = rng.uniform(0.01, 2.0, n).astype(np.float32)
+    sw = rng.uniform(1e-3, 1e-2, N).astype(np.float32)
+    a_dev = torch.from_numpy(packing.pack(qa, bits)).cuda()
+    w_dev = torch.from_numpy(packing.pack(qw, bits)).cuda()
+    y = torch.empty((n, N), dtype=torch.bfloat16, device="cuda")
+    rsq.rsq_qgemm(a_dev, to_dev(sa, "f32"), n, w_dev, to_dev(sw, "f32"), N, K, bits, y)
+    y2 = torch.empty_like(y)
+    acc = torch.empty((n, N), dtype=torch.int32, device="cuda")
+    rsq.rsq_qgemm(a_dev, to_dev(sa, "f32"), n, w_dev, to_dev(sw, "f32"), N, K, bits, y2, acc_out=acc)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2)
+    rows = np.unique(np.r_[0, 255, 256, n - 1, rng.choice(n, 40, replace=False)])
+    cols = np.unique(np.r_[0, 255, 256, N - 33, N - 1, rng.choice(N, 120, replace=False)])
+    acc_ref = online.gemm(qa[rows], qw[cols])
+    acc_gpu = acc[torch.from_numpy(rows).cuda()][:, torch.from_numpy(cols).cuda()].cpu().numpy().astype(np.int64)
+    assert np.array_equal(acc_gpu, acc_ref)
+    y_gpu = to_host(y[torch.from_numpy(rows).cuda()][:, torch.from_numpy(cols).cuda()])
+    assert np.array_equal(np.asarray(y_gpu, np.float64), np.asarray(online.dequant(acc_ref, sa[rows], sw[cols], "bf16"), np.float64))
+
+
 def test_qgemm_strided_output_and_minimum_codes():
     rsq = lib()
     import torch
