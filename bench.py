@@ -23,11 +23,14 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix-core peak
 INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 matrix-core peak
 METRIC = "tokens/s per decoder-layer linear path (W4A4, D=4096, r=32); % HBM / MFMA peak"
 
@@ -41,6 +44,9 @@ def parse():
     p.add_argument("--copies", type=int, default=2)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample", type=int, default=16, help="tokens in the CPU oracle sample")
+    p.add_argument("--no-dense", action="store_true", help="skip the dense h T comparator")
+    p.add_argument("--rank-sweep", action="store_true",
+                   help="only the correction at every rank of the workload (time and error against dense h T)")
     p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                    help="only run a plain device copy of MIB MiB (calibrates rocprofv3 byte counters) and exit")
     return p.parse_args()
@@ -61,6 +67,90 @@ def copy_probe(mib: int) -> None:
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_probe_bytes_read": nbytes, "copy_probe_bytes_written": nbytes, "dispatches": 3}))
+
+
+def _time_ms(fn, iters: int, stream) -> float:
+    import torch
+    for _ in range(3):
+        fn()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(iters):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / iters
+
+
+def dense_comparator(path, which: str = "A", iters: int = 20):
+    """The dense alternative at one junction: h T as a D x D bf16 GEMM (the vendor
+    library's, through torch) beside the rank-r correction kernel, and how far
+    the correction is from the dense product."""
+    import torch
+    import rotation_bit_post_amd as B
+    t32 = path.mismatch[which]
+    h = path.bufs["h"]
+    n, d = h.shape
+    site = path.sites[which]
+    stream = torch.cuda.current_stream()
+    t_dev = torch.from_numpy(t32).to(device="cuda", dtype=h.dtype)
+    dense = torch.empty_like(h)
+    corr = torch.empty_like(h)
+    ms_dense = _time_ms(lambda: torch.matmul(h, t_dev, out=dense), iters, stream)
+    ms_corr = _time_ms(lambda: B.rsq_subspace_correct(h, corr, site.buf, site.r), iters, stream)
+    ref = h.float() @ torch.from_numpy(t32).cuda()
+    err_corr = float(torch.linalg.vector_norm(corr.float() - ref) / torch.linalg.vector_norm(ref))
+    err_dense = float(torch.linalg.vector_norm(dense.float() - ref) / torch.linalg.vector_norm(ref))
+    flops = 2.0 * n * d * d
+    return {
+        "junction": f"site {which}, {n} tokens, D={d}, r={site.r}, {str(h.dtype).split('.')[-1]}",
+        "dense_ms": round(ms_dense, 5),
+        "dense_tflops": round(flops / (ms_dense * 1e-3) / 1e12, 1),
+        "dense_frac_bf16_peak": round(flops / (ms_dense * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+        "correction_ms": round(ms_corr, 5),
+        "speedup_vs_dense": round(ms_dense / ms_corr, 2),
+        "correction_rel_l2_vs_dense_fp32": round(err_corr, 5),
+        "dense_bf16_rel_l2_vs_dense_fp32": round(err_dense, 6),
+        "note": "dense h T by the vendor bf16 GEMM (hipBLASLt through torch.matmul), for comparison only; "
+                "the rank-r correction's distance from h T is the approximation the method makes",
+    }
+
+
+def rank_sweep(cid: int, iters: int = 20):
+    """Correction time and distance from dense h T at every rank of the workload."""
+    import torch
+    import rotation_bit_post_amd as B
+    from rotation_bit_post_amd import offline
+    from rotation_bit_post_amd.path import make_site, synthetic_mismatch
+    import synth
+    cfg = synth.CONFIGS[cid]
+    ranks = cfg.ranks or (cfg.r,)
+    progress(f"rank sweep on workload {cid}: ranks {ranks}")
+    t = synthetic_mismatch(cfg, "A")
+    h = synth.residual(cfg)
+    hd = torch.from_numpy(h).cuda()
+    hd = hd.to(torch.bfloat16) if cfg.h_dtype == "bf16" else hd
+    ref = hd.float() @ torch.from_numpy(t.astype(np.float32)).cuda()
+    stream = torch.cuda.current_stream()
+    rows = []
+    for r in ranks:
+        U, M = offline.convert_mismatch(t, r)
+        site = make_site(U, M)
+        out = torch.empty_like(hd)
+        codes = torch.empty((cfg.n, B.rsq_packed_row_bytes(cfg.D, cfg.bits)), dtype=torch.uint8, device="cuda")
+        scales = torch.empty(cfg.n, dtype=torch.float32, device="cuda")
+        ms_c = _time_ms(lambda: B.rsq_subspace_correct(hd, out, site.buf, r), iters, stream)
+        ms_q = _time_ms(lambda: B.rsq_correct_quant(hd, out, site.buf, r, codes, scales, cfg.bits), iters, stream)
+        B.rsq_subspace_correct(hd, out, site.buf, r)
+        err = float(torch.linalg.vector_norm(out.float() - ref) / torch.linalg.vector_norm(ref))
+        rows.append({"r": r, "correction_ms": round(ms_c, 5), "correction_norm_quant_ms": round(ms_q, 5),
+                     "rel_l2_vs_dense_hT": round(err, 5)})
+        progress(f"r={r}: {ms_c * 1e3:.1f} us, error {err:.4f}")
+    print(json.dumps({"rank_sweep": rows, "workload": f"{cfg.name}: D={cfg.D}, {cfg.n} tokens, {cfg.h_dtype}",
+                      "note": "error of the rank-r correction against the dense product h T (float32); "
+                              "the synthetic rotations are far from I, so the error falls slowly with r"}),
+          flush=True)
 
 
 def kernel_source_hash() -> str:
@@ -121,11 +211,14 @@ def main():
     if args.copy_probe:
         copy_probe(args.copy_probe)
         return
+    if args.rank_sweep:
+        rank_sweep(args.config)
+        return
     from rotation_bit_post_amd.path import LayerPath
 
     t_build = time.perf_counter()
     progress(f"building config {args.config} (sites, weights, inputs)")
-    base = LayerPath.build(args.config)
+    base = LayerPath.build(args.config, keep_mismatch=not args.no_dense)
     copies = [base] + [base.clone() for _ in range(args.copies - 1)]
     torch.cuda.synchronize()
     t_build = time.perf_counter() - t_build
@@ -172,6 +265,22 @@ def main():
     e1.record(stream)
     torch.cuda.synchronize()
     ms_off = e0.elapsed_time(e1) / args.steps
+
+    # the chained layer: residual adds fused into the o / down GEMMs, site B reads h2
+    ms_chain = None
+    if "B" in base.sites:
+        chain_lists = [p.stages(correction=True, chain=True) for p in copies]
+        for i in range(args.warmup):
+            for _, _, fn in chain_lists[i % len(copies)]:
+                fn()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(args.steps):
+            for _, _, fn in chain_lists[i % len(copies)]:
+                fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms_chain = e0.elapsed_time(e1) / args.steps
 
     stages_out = {}
     gemm_ops = gemm_ms = gemm_launches = 0
@@ -228,10 +337,20 @@ def main():
             "overhead_frac": round(ms_per_step / ms_off - 1.0, 4),
             "note": "same path with each site reduced to RMSNorm + quantisation (T = I, a single global rotation)",
         },
+        "layer_chained": None if ms_chain is None else {
+            "ms_per_step": round(ms_chain, 5),
+            "tokens_per_s": round(n / (ms_chain * 1e-3), 1),
+            "note": "the same eight stages with the residual stream carried through: o_proj and down_proj "
+                    "outputs added to the corrected residual inside the GEMM epilogue (rsq_qgemm_residual), "
+                    "site B reading h2; timed back to back, no events between stages",
+        },
         "wall_s_timed": round(wall, 3),
         "setup_s": round(t_build, 1),
         "kernel_source_hash": src_hash,
     }
+    if not args.no_dense and "A" in base.mismatch:
+        progress("dense h T comparator")
+        out["dense_T_comparator"] = dense_comparator(base)
     if not args.no_cpu_baseline:
         progress(f"CPU oracle on a {args.cpu_sample}-token sample")
         out["cpu_baseline"] = cpu_baseline(base, args.cpu_sample)

@@ -143,6 +143,20 @@ rsq_status rsq_qgemm(const uint8_t *a_codes, const float *a_scales, int64_t n,
                      int32_t *acc_out, void *stream);
 
 /*
+ * Quantised linear plus a residual: the residual adds around the attention
+ * and FFN blocks, whose junctions carry the corrections (zh 2.1; fr 2B),
+ * fused into the linear's output so that the o_proj and down_proj results
+ * land on the residual stream in one pass:
+ *   y[t, j] = y_dtype(v + float32(residual[t, j])),  v as in rsq_qgemm (float32)
+ * residual: n rows of n_out values of y_dtype, row stride ld_r; it may be y
+ * itself (in place, ld_r == ld_y); any other overlap is an error.
+ */
+rsq_status rsq_qgemm_residual(const uint8_t *a_codes, const float *a_scales, int64_t n,
+                              const uint8_t *w_codes, const float *w_scales, int64_t n_out,
+                              int64_t k, int bits, const void *residual, int64_t ld_r,
+                              void *y, int y_dtype, int64_t ld_y, void *stream);
+
+/*
  * One correction site feeding its quantised linear: rsq_correct_quant then
  * rsq_qgemm on its codes. Writes h_out, codes, scales and y (stride n_out).
  */

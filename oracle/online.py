@@ -111,6 +111,22 @@ def dequant(acc, s_a, s_w, out_dtype: str):
     return round_to_bf16(y.astype(np.float64))
 
 
+def dequant_add(acc, s_a, s_w, residual, out_dtype: str):
+    """y = out_dtype(v + float32(residual)) with v = (float32(acc) * s_a[t]) * s_w[j] in float32.
+
+    The residual add of a decoder block (the junction structure: zh §2.1;
+    fr §2B) taken into the linear's output, rounded once.
+    """
+    acc = np.asarray(acc, np.int64)
+    if np.any(np.abs(acc) >= 2 ** 24):
+        raise ValueError("accumulator not exactly representable in float32")
+    v = (acc.astype(np.float32) * np.asarray(s_a, np.float32)[:, None]) * np.asarray(s_w, np.float32)[None, :]
+    y = v + np.asarray(residual, np.float32)
+    if out_dtype == "f32":
+        return y
+    return round_to_bf16(y.astype(np.float64))
+
+
 # ------------------------------------------------ entry points on packed data
 def subspace_correct(h, u, m, dtype: str):
     return correct(h, u, m, dtype)
@@ -126,6 +142,11 @@ def qgemm_packed(a_codes, a_scales, w_codes, w_scales, k: int, bits: int, y_dtyp
     qw = unpack(w_codes, k, bits)
     acc = gemm(qa, qw)
     return dequant(acc, a_scales, w_scales, y_dtype), acc
+
+
+def qgemm_residual_packed(a_codes, a_scales, w_codes, w_scales, k: int, bits: int, residual, y_dtype: str):
+    acc = gemm(unpack(a_codes, k, bits), unpack(w_codes, k, bits))
+    return dequant_add(acc, a_scales, w_scales, residual, y_dtype), acc
 
 
 def layer_fused(h, u, m, h_dtype: str, bits: int, eps: float, w_codes, w_scales,
@@ -156,4 +177,27 @@ def layer_linear_path(h, site_a, site_b, weights, o_in, down_in, h_dtype, bits, 
     f = np.asarray(down_in).shape[1]
     dc, ds, _ = quant_act_packed(down_in, bits, False)
     out["down"] = qgemm_packed(dc, ds, *weights["down"], f, bits, y_dtype)[0]
+    return out
+
+
+def layer_chained(h, site_a, site_b, weights, o_in, down_in, h_dtype, bits, eps, y_dtype):
+    """One decoder layer with its residual stream carried through (two sites).
+
+    h_a = correct_A(h); q|k|v from h_a; h2 = h_a + o_proj(o_in);
+    h_b = correct_B(h2); gate|up from h_b; h3 = h_b + down_proj(down_in).
+    The attention core and SiLU * up are stood in for by o_in and down_in;
+    each residual add is rounded once to the residual's dtype. h3 is the next
+    layer's input.
+    """
+    d = np.asarray(h).shape[1]
+    out = {}
+    a = layer_fused(h, *site_a, h_dtype, bits, eps, *weights["qkv"], y_dtype)
+    out["siteA"], out["qkv"] = a, a["y"]
+    oc, os_, _ = quant_act_packed(o_in, bits, False)
+    out["h2"] = qgemm_residual_packed(oc, os_, *weights["o"], d, bits, a["h_out"], h_dtype)[0]
+    b = layer_fused(out["h2"], *site_b, h_dtype, bits, eps, *weights["gate_up"], y_dtype)
+    out["siteB"], out["gate_up"] = b, b["y"]
+    f = np.asarray(down_in).shape[1]
+    dc, ds, _ = quant_act_packed(down_in, bits, False)
+    out["h3"] = qgemm_residual_packed(dc, ds, *weights["down"], f, bits, b["h_out"], h_dtype)[0]
     return out

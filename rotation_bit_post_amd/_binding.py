@@ -47,6 +47,7 @@ def _load() -> C.CDLL:
         "rsq_quant_act": (i32, [vp, i32, i64, i64, i64, C.c_uint, vp, f32, i32, vp, vp, vp]),
         "rsq_correct_quant": (i32, [vp, vp, i32, i64, i64, vp, i32, vp, f32, i32, vp, vp, vp]),
         "rsq_qgemm": (i32, [vp, vp, i64, vp, vp, i64, i64, i32, vp, i32, i64, vp, vp]),
+        "rsq_qgemm_residual": (i32, [vp, vp, i64, vp, vp, i64, i64, i32, vp, i64, vp, i32, i64, vp]),
         "rsq_layer_fused": (i32, [vp, vp, i32, i64, i64, vp, i32, vp, f32, i32, vp, vp, vp, vp, i64, vp, i32, vp]),
     }
     for name, (res, args) in sig.items():
@@ -57,7 +58,7 @@ def _load() -> C.CDLL:
 
 LIB = _load()
 EXPORTS = ("rsq_version", "rsq_status_str", "rsq_last_error", "rsq_packed_row_bytes", "rsq_site_bytes",
-           "rsq_site_prepare", "rsq_subspace_correct", "rsq_quant_act", "rsq_correct_quant", "rsq_qgemm",
+           "rsq_site_prepare", "rsq_subspace_correct", "rsq_quant_act", "rsq_correct_quant", "rsq_qgemm", "rsq_qgemm_residual",
            "rsq_layer_fused")
 
 
@@ -138,6 +139,16 @@ def rsq_qgemm(a_codes, a_scales, n: int, w_codes, w_scales, n_out: int, k: int, 
               stream=None) -> None:
     _check(LIB.rsq_qgemm(_ptr(a_codes), _ptr(a_scales), n, _ptr(w_codes), _ptr(w_scales), n_out, k, bits,
                          _ptr(y), _dtype_code(y), y.stride(0), _ptr(acc_out), _stream(stream)), "rsq_qgemm")
+
+
+def rsq_qgemm_residual(a_codes, a_scales, n: int, w_codes, w_scales, n_out: int, k: int, bits: int, residual, y,
+                       stream=None) -> None:
+    """y = dequantised quantised linear + residual (residual may be y itself)."""
+    if residual.dtype != y.dtype:
+        raise ValueError("residual and y must have the same dtype")
+    _check(LIB.rsq_qgemm_residual(_ptr(a_codes), _ptr(a_scales), n, _ptr(w_codes), _ptr(w_scales), n_out, k, bits,
+                                  _ptr(residual), residual.stride(0), _ptr(y), _dtype_code(y), y.stride(0),
+                                  _stream(stream)), "rsq_qgemm_residual")
 
 
 def rsq_layer_fused(h_in, h_out, site, r: int, codes, scales, w_codes, w_scales, n_out: int, y, bits: int,

@@ -190,8 +190,42 @@ rsq_status rsq_qgemm(const uint8_t *a_codes, const float *a_scales, int64_t n, c
               RSQ_ERR_INVALID_ARG, "operands must be 16-byte aligned");
     RSQ_CHECK(acc_out == nullptr || aligned16(acc_out), RSQ_ERR_INVALID_ARG, "acc_out must be 16-byte aligned");
     return hip_status(rsq::launch_qgemm(a_codes, a_scales, n, w_codes, w_scales, n_out, k, bits, y, y_dtype, ld_y,
-                                        acc_out, static_cast<hipStream_t>(stream)),
+                                        acc_out, nullptr, 0, static_cast<hipStream_t>(stream)),
                       "rsq_qgemm launch");
+}
+
+rsq_status rsq_qgemm_residual(const uint8_t *a_codes, const float *a_scales, int64_t n, const uint8_t *w_codes,
+                              const float *w_scales, int64_t n_out, int64_t k, int bits, const void *residual,
+                              int64_t ld_r, void *y, int y_dtype, int64_t ld_y, void *stream) {
+    g_last_error[0] = 0;
+    rsq_status st = check_bits(bits);
+    if (st != RSQ_OK) return st;
+    RSQ_CHECK(dtype_ok(y_dtype), RSQ_ERR_INVALID_ARG, "y_dtype = %d is not RSQ_F32 or RSQ_BF16", y_dtype);
+    RSQ_CHECK(n >= 0, RSQ_ERR_INVALID_ARG, "n = %lld is negative", (long long)n);
+    RSQ_CHECK(n_out > 0 && n_out % 32 == 0, RSQ_ERR_INVALID_ARG, "n_out = %lld must be a positive multiple of 32", (long long)n_out);
+    RSQ_CHECK(k > 0 && k % 32 == 0, RSQ_ERR_INVALID_ARG, "k = %lld must be a positive multiple of 32", (long long)k);
+    RSQ_CHECK(k <= 65536, RSQ_ERR_UNSUPPORTED, "k = %lld exceeds 65536 (int32 accumulator bound)", (long long)k);
+    RSQ_CHECK(ld_y >= n_out, RSQ_ERR_INVALID_ARG, "ld_y = %lld < n_out = %lld", (long long)ld_y, (long long)n_out);
+    RSQ_CHECK(ld_r >= n_out, RSQ_ERR_INVALID_ARG, "ld_r = %lld < n_out = %lld", (long long)ld_r, (long long)n_out);
+    RSQ_CHECK(n <= 0x7fffffff && n_out <= 0x7fffffff, RSQ_ERR_UNSUPPORTED, "size too large");
+    if (n == 0) return RSQ_OK;
+    RSQ_CHECK(a_codes && a_scales && w_codes && w_scales && y && residual, RSQ_ERR_INVALID_ARG, "null pointer");
+    RSQ_CHECK(aligned16(a_codes) && aligned16(w_codes) && aligned16(a_scales) && aligned16(w_scales) && aligned16(y) &&
+                  aligned16(residual),
+              RSQ_ERR_INVALID_ARG, "operands must be 16-byte aligned");
+    if (residual != y) {
+        const size_t es = dtype_size(y_dtype);
+        const char *a = static_cast<const char *>(residual), *b = static_cast<const char *>(y);
+        const size_t span_r = static_cast<size_t>((n - 1) * ld_r + n_out) * es;
+        const size_t span_y = static_cast<size_t>((n - 1) * ld_y + n_out) * es;
+        RSQ_CHECK(a + span_r <= b || b + span_y <= a, RSQ_ERR_INVALID_ARG,
+                  "residual and y overlap without being the same buffer");
+    } else {
+        RSQ_CHECK(ld_r == ld_y, RSQ_ERR_INVALID_ARG, "in place (residual == y) needs ld_r == ld_y");
+    }
+    return hip_status(rsq::launch_qgemm(a_codes, a_scales, n, w_codes, w_scales, n_out, k, bits, y, y_dtype, ld_y,
+                                        nullptr, residual, ld_r, static_cast<hipStream_t>(stream)),
+                      "rsq_qgemm_residual launch");
 }
 
 rsq_status rsq_layer_fused(const void *h_in, void *h_out, int h_dtype, int64_t n, int64_t d, const void *site, int r,
@@ -216,7 +250,7 @@ rsq_status rsq_layer_fused(const void *h_in, void *h_out, int h_dtype, int64_t n
                     "rsq_layer_fused correction launch");
     if (st != RSQ_OK) return st;
     return hip_status(rsq::launch_qgemm(codes, scales, n, w_codes, w_scales, n_out, d, bits, y, y_dtype, n_out,
-                                        nullptr, s),
+                                        nullptr, nullptr, 0, s),
                       "rsq_layer_fused GEMM launch");
 }
 

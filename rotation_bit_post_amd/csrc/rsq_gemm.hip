@@ -40,6 +40,8 @@ template <> __device__ __forceinline__ float to_out<float>(float v) { return v; 
 template <> __device__ __forceinline__ uint16_t to_out<uint16_t>(float v) {
     return static_cast<uint16_t>(pk_bf16(v, 0.0f));  // nearest even, one instruction
 }
+__device__ __forceinline__ float from_out(float v) { return v; }
+__device__ __forceinline__ float from_out(uint16_t v) { return bf16_to_f32(v); }
 
 // One group of 32 packed codes, as loaded from HBM.
 template <int BITS> struct Group;
@@ -220,7 +222,8 @@ __global__ __launch_bounds__(WM * WN * 64) void qgemm_kernel(const uint8_t *__re
                                                              const uint8_t *__restrict__ W,
                                                              const float *__restrict__ sw, int N, int K,
                                                              YT *__restrict__ y, int64_t ld_y,
-                                                             int32_t *__restrict__ acc_out) {
+                                                             int32_t *__restrict__ acc_out,
+                                                             const YT *__restrict__ res, int64_t ld_r) {
     using T = GemmTile<BITS, BM, BN, WM, WN, P>;
     using F = Fmt<BITS>;
     constexpr int TM = T::TM, TN = T::TN;
@@ -265,8 +268,10 @@ __global__ __launch_bounds__(WM * WN * 64) void qgemm_kernel(const uint8_t *__re
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
                     const int tl = wm * (BM / WM) + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
+                    const bool in = bm0 + tl < n && bn0 + cl < N;
                     const float sat = bm0 + tl < n ? sa[bm0 + tl] : 0.0f;
-                    const float val = (static_cast<float>(acc[i][j][v] >> F::kShift) * sat) * swj;
+                    float val = (static_cast<float>(acc[i][j][v] >> F::kShift) * sat) * swj;
+                    if (res != nullptr && in) val += from_out(res[static_cast<int64_t>(bm0 + tl) * ld_r + bn0 + cl]);
                     ot[tl * OS + cl] = to_out<uint16_t>(val);
                 }
             }
@@ -293,7 +298,8 @@ __global__ __launch_bounds__(WM * WN * 64) void qgemm_kernel(const uint8_t *__re
                 const int tok = bm0 + wm * (BM / WM) + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
                 if (cvalid && tok < n) {
                     const int a = acc[i][j][v] >> F::kShift;
-                    const float val = (static_cast<float>(a) * sa[tok]) * swj;
+                    float val = (static_cast<float>(a) * sa[tok]) * swj;
+                    if (res != nullptr) val += from_out(res[static_cast<int64_t>(tok) * ld_r + ch]);
                     y[static_cast<int64_t>(tok) * ld_y + ch] = to_out<YT>(val);
                     if (acc_out != nullptr) acc_out[static_cast<int64_t>(tok) * N + ch] = a;
                 }
@@ -304,11 +310,11 @@ __global__ __launch_bounds__(WM * WN * 64) void qgemm_kernel(const uint8_t *__re
 
 template <int BITS, int BM, int BN, int WM, int WN, typename YT, int P = 2>
 hipError_t launch_t(const uint8_t *a, const float *sa, int64_t n, const uint8_t *w, const float *sw, int64_t N,
-                    int64_t K, void *y, int64_t ld_y, int32_t *acc_out, hipStream_t s) {
+                    int64_t K, void *y, int64_t ld_y, int32_t *acc_out, const void *res, int64_t ld_r, hipStream_t s) {
     const int64_t mt = (n + BM - 1) / BM, nt = (N + BN - 1) / BN;
     hipLaunchKernelGGL((qgemm_kernel<BITS, BM, BN, WM, WN, P, YT>), dim3(static_cast<unsigned>(mt * nt)),
                        dim3(WM * WN * 64), 0, s, a, sa, static_cast<int>(n), w, sw, static_cast<int>(N),
-                       static_cast<int>(K), static_cast<YT *>(y), ld_y, acc_out);
+                       static_cast<int>(K), static_cast<YT *>(y), ld_y, acc_out, static_cast<const YT *>(res), ld_r);
     return hipGetLastError();
 }
 
@@ -319,31 +325,31 @@ hipError_t launch_t(const uint8_t *a, const float *sa, int64_t n, const uint8_t 
 // small batches spread over the CUs.
 template <int BITS, typename YT>
 hipError_t launch_b(const uint8_t *a, const float *sa, int64_t n, const uint8_t *w, const float *sw, int64_t N,
-                    int64_t K, void *y, int64_t ld_y, int32_t *acc_out, hipStream_t s) {
-    if (n <= 32) return launch_t<BITS, 32, 128, 1, 4, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, s);
-    if (n <= 64) return launch_t<BITS, 64, 128, 2, 2, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, s);
+                    int64_t K, void *y, int64_t ld_y, int32_t *acc_out, const void *res, int64_t ld_r, hipStream_t s) {
+    if (n <= 32) return launch_t<BITS, 32, 128, 1, 4, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s);
+    if (n <= 64) return launch_t<BITS, 64, 128, 2, 2, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s);
     const int64_t cus = device_cus();
     const int64_t mt = (n + 255) / 256;
     const int64_t rounds_128 = (mt * ((N + 127) / 128) + cus - 1) / cus;
     const int64_t rounds_256 = (mt * ((N + 255) / 256) + cus - 1) / cus;
     if (n >= 256 && 18 * rounds_256 < 10 * rounds_128)
-        return launch_t<BITS, 256, 256, 4, 2, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, s);
+        return launch_t<BITS, 256, 256, 4, 2, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s);
     if (n >= 256 && mt * ((N + 127) / 128) >= 200)
-        return launch_t<BITS, 256, 128, 4, 2, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, s);
-    return launch_t<BITS, 128, 128, 2, 2, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, s);
+        return launch_t<BITS, 256, 128, 4, 2, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s);
+    return launch_t<BITS, 128, 128, 2, 2, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s);
 }
 
 }  // namespace
 
 hipError_t launch_qgemm(const uint8_t *a, const float *sa, int64_t n, const uint8_t *w, const float *sw,
                         int64_t n_out, int64_t k, int bits, void *y, int y_dtype, int64_t ld_y,
-                        int32_t *acc_out, hipStream_t s) {
+                        int32_t *acc_out, const void *res, int64_t ld_r, hipStream_t s) {
     if (bits == 4) {
-        if (y_dtype == 1) return launch_b<4, uint16_t>(a, sa, n, w, sw, n_out, k, y, ld_y, acc_out, s);
-        return launch_b<4, float>(a, sa, n, w, sw, n_out, k, y, ld_y, acc_out, s);
+        if (y_dtype == 1) return launch_b<4, uint16_t>(a, sa, n, w, sw, n_out, k, y, ld_y, acc_out, res, ld_r, s);
+        return launch_b<4, float>(a, sa, n, w, sw, n_out, k, y, ld_y, acc_out, res, ld_r, s);
     }
-    if (y_dtype == 1) return launch_b<3, uint16_t>(a, sa, n, w, sw, n_out, k, y, ld_y, acc_out, s);
-    return launch_b<3, float>(a, sa, n, w, sw, n_out, k, y, ld_y, acc_out, s);
+    if (y_dtype == 1) return launch_b<3, uint16_t>(a, sa, n, w, sw, n_out, k, y, ld_y, acc_out, res, ld_r, s);
+    return launch_b<3, float>(a, sa, n, w, sw, n_out, k, y, ld_y, acc_out, res, ld_r, s);
 }
 
 }  // namespace rsq

@@ -32,8 +32,10 @@ hipError_t launch_quant(const void *x, int x_dtype, int64_t n, int k, int64_t ld
                         const float *norm_w, float eps, int bits, uint8_t *codes, float *scales,
                         hipStream_t s);
 
+// res: NULL, or n rows of n_out values of the output type (stride ld_r) added
+// to the dequantised result before its rounding.
 hipError_t launch_qgemm(const uint8_t *a, const float *sa, int64_t n, const uint8_t *w, const float *sw,
                         int64_t n_out, int64_t k, int bits, void *y, int y_dtype, int64_t ld_y,
-                        int32_t *acc_out, hipStream_t s);
+                        int32_t *acc_out, const void *res, int64_t ld_r, hipStream_t s);
 
 }  // namespace rsq

@@ -43,9 +43,18 @@ def synthetic_rotation(a: np.ndarray, eps: float) -> np.ndarray:
     return sylvester_hadamard(a.shape[0]) @ cayley_rotation(a, eps)
 
 
+def mismatch(r_in: np.ndarray, r_out: np.ndarray) -> np.ndarray:
+    """T = R_out^T R_in, the rotation a junction between the two bases needs."""
+    return r_out.T @ r_in
+
+
 def convert_site(r_in: np.ndarray, r_out: np.ndarray, r: int):
     """(U_r, M) in float32 for a junction with rotations r_in (input) and r_out (output)."""
-    t = r_out.T @ r_in
+    return convert_mismatch(mismatch(r_in, r_out), r)
+
+
+def convert_mismatch(t: np.ndarray, r: int):
+    """(U_r, M) in float32 from the mismatch T (float64, orthogonal)."""
     d = t.shape[0]
     if not 1 <= r <= d:
         raise ValueError("rank out of range")

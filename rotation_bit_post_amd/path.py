@@ -81,13 +81,16 @@ def quantize_weight_on_device(w: np.ndarray, bits: int, name: str = "") -> QLine
     return QLinear(name, N, K, codes, scales)
 
 
+def synthetic_mismatch(cfg: Config, which: str) -> np.ndarray:
+    """T (float64) of a synthetic site: rotations H C(eps A) from the seeded skew generators."""
+    r_in = offline.synthetic_rotation(G.skew_generator(cfg, which, "in"), cfg.eps_rot)
+    r_out = offline.synthetic_rotation(G.skew_generator(cfg, which, "out"), cfg.eps_rot)
+    return offline.mismatch(r_in, r_out)
+
+
 def synthetic_site(cfg: Config, which: str, r: int):
-    """(U_r, M) of a synthetic site: rotations H C(eps A) from the seeded skew generators."""
-    a_in = G.skew_generator(cfg, which, "in")
-    a_out = G.skew_generator(cfg, which, "out")
-    r_in = offline.synthetic_rotation(a_in, cfg.eps_rot)
-    r_out = offline.synthetic_rotation(a_out, cfg.eps_rot)
-    return offline.convert_site(r_in, r_out, r)
+    """(U_r, M) of a synthetic site."""
+    return offline.convert_mismatch(synthetic_mismatch(cfg, which), r)
 
 
 @dataclass
@@ -100,14 +103,16 @@ class LayerPath:
     sites: dict = field(default_factory=dict)
     linears: dict = field(default_factory=dict)
     bufs: dict = field(default_factory=dict)
+    mismatch: dict = field(default_factory=dict)   # site -> T (float32), kept on request
 
     @classmethod
     def build(cls, cid: int, n: int | None = None, r: int | None = None, gqa: bool = True,
-              sites=None, weights=None) -> "LayerPath":
+              sites=None, weights=None, keep_mismatch: bool = False) -> "LayerPath":
         """Device-resident inputs and outputs of one layer path.
 
         sites: optional {"A": (U, M), "B": (U, M)}; weights: optional
         {linear name: float32 (N, K)} - both default to the seeded synthetic ones.
+        keep_mismatch: also keep each synthetic site's dense T (for comparisons).
         """
         cfg = CONFIGS[cid]
         self = cls(cfg, n or cfg.n, r or cfg.r, gqa)
@@ -115,7 +120,14 @@ class LayerPath:
         names = sorted({l.source for l in lins if l.source.startswith("site")})
         for src in names:
             which = src[-1]
-            U, M = sites[which] if sites is not None else synthetic_site(cfg, which, self.r)
+            if sites is not None:
+                U, M = sites[which]
+            else:
+                t = synthetic_mismatch(cfg, which)
+                U, M = offline.convert_mismatch(t, self.r)
+                if keep_mismatch:
+                    self.mismatch[which] = t.astype(np.float32)
+                del t
             self.sites[which] = make_site(U, M)
         for lin in lins:
             if weights is not None:
@@ -146,6 +158,10 @@ class LayerPath:
         self.bufs["h"] = _dev_bf16(h) if hdt == torch.bfloat16 else _dev(h)
         for which in self.sites:
             self.bufs[f"h_{which}"] = torch.empty_like(self.bufs["h"])
+        if "B" in self.sites:   # residual stream after the attention and after the FFN block
+            self.bufs["h2"] = torch.empty_like(self.bufs["h"])
+            self.bufs["h3"] = torch.empty_like(self.bufs["h"])
+        for which in self.sites:
             self.bufs[f"codes_{which}"] = torch.empty((n, B.rsq_packed_row_bytes(cfg.D, bits)), dtype=torch.uint8, device="cuda")
             self.bufs[f"scales_{which}"] = torch.empty(n, dtype=torch.float32, device="cuda")
         for name, lin in self.linears.items():
@@ -157,9 +173,18 @@ class LayerPath:
                 self.bufs[f"scales_{lin.source}"] = torch.empty(n, dtype=torch.float32, device="cuda")
 
     # ------------------------------------------------------------------ run
-    def stages(self, correction: bool = True):
-        """The path as a list of (stage name, kind, callable); kind is "site", "quant" or "gemm"."""
+    def stages(self, correction: bool = True, chain: bool = False):
+        """The path as a list of (stage name, kind, callable); kind is "site", "quant" or "gemm".
+
+        chain: carry the residual stream through the layer - the o_proj output
+        is added to site A's corrected residual (giving h2, site B's input) and
+        the down_proj output to site B's (giving h3, the next layer's input),
+        both inside the GEMM epilogue. Without it, site B reads site A's output
+        and the o / down outputs are separate tensors.
+        """
         cfg, bits, b = self.cfg, self.cfg.bits, self.bufs
+        if chain and "B" not in self.sites:
+            raise ValueError("a chained layer needs both sites")
         out = []
         h_cur = b["h"]
         order = ["A", "B"] if "B" in self.sites else ["A"]
@@ -185,8 +210,18 @@ class LayerPath:
                     x, c, s = b[stand_in], b[f"codes_{stand_in}"], b[f"scales_{stand_in}"]
                     out.append((f"quant_{stand_in}", "quant",
                                 lambda x=x, c=c, s=s: B.rsq_quant_act(x, c, s, bits, rmsnorm=False)))
-                    out.append(self._gemm(lin, c, s))
+                    if chain:
+                        dst = b["h2"] if which == "A" else b["h3"]
+                        out.append(self._gemm_residual(lin, c, s, h_cur, dst))
+                        h_cur = dst
+                    else:
+                        out.append(self._gemm(lin, c, s))
         return out
+
+    def _gemm_residual(self, lin: QLinear, codes, scales, residual, dst):
+        n, bits = self.n, self.cfg.bits
+        return (f"gemm_{lin.name}_res", "gemm",
+                lambda: B.rsq_qgemm_residual(codes, scales, n, lin.codes, lin.scales, lin.N, lin.K, bits, residual, dst))
 
     def _gemm(self, lin: QLinear, codes, scales):
         y = self.bufs[f"y_{lin.name}"]
@@ -194,8 +229,8 @@ class LayerPath:
         return (f"gemm_{lin.name}", "gemm",
                 lambda: B.rsq_qgemm(codes, scales, n, lin.codes, lin.scales, lin.N, lin.K, bits, y))
 
-    def step(self, correction: bool = True):
-        for _, _, fn in self.stages(correction):
+    def step(self, correction: bool = True, chain: bool = False):
+        for _, _, fn in self.stages(correction, chain):
             fn()
 
     # -------------------------------------------------- algorithmic work
@@ -210,6 +245,9 @@ class LayerPath:
         if name.startswith("quant_"):
             k = self.linears["o"].K if name == "quant_o_in" else self.linears["down"].K
             return (n * (k * hs + k * bits // 8 + 4), 0)
-        lin = self.linears[name[len("gemm_"):]]
+        res = name.endswith("_res")
+        lin = self.linears[name[len("gemm_"):len(name) - (4 if res else 0)]]
         byts = lin.N * lin.K * bits // 8 + 4 * lin.N + n * (lin.K * bits // 8 + 4) + n * lin.N * ys
+        if res:
+            byts += n * lin.N * hs   # the residual read beside the output write
         return (byts, 2 * n * lin.N * lin.K)

@@ -109,6 +109,19 @@ def test_qgemm_validation(args, status, needle):
     assert st == status and needle in msg, (st, msg)
 
 
+def test_qgemm_residual_validation():
+    # (a, sa, n, w, sw, n_out, k, bits, residual, ld_r, y, y_dtype, ld_y, stream)
+    st, msg = _call("rsq_qgemm_residual", FAKE, FAKE, 4, FAKE, FAKE, 128, 256, 4, None, 128, FAKE, 1, 128, None)
+    assert st == 1 and "null" in msg
+    st, msg = _call("rsq_qgemm_residual", FAKE, FAKE, 4, FAKE, FAKE, 128, 256, 4, FAKE, 64, FAKE + 4096, 1, 128, None)
+    assert st == 1 and "ld_r" in msg
+    st, msg = _call("rsq_qgemm_residual", FAKE, FAKE, 4, FAKE, FAKE, 128, 256, 4, FAKE, 128, FAKE + 64, 1, 128, None)
+    assert st == 1 and "overlap" in msg
+    st, msg = _call("rsq_qgemm_residual", FAKE, FAKE, 4, FAKE, FAKE, 128, 256, 4, FAKE, 160, FAKE, 1, 128, None)
+    assert st == 1 and "in place" in msg
+    assert _call("rsq_qgemm_residual", None, None, 0, None, None, 128, 256, 4, None, 128, None, 1, 128, None)[0] == 0
+
+
 def test_empty_batches_are_accepted_without_pointers():
     # n = 0 enqueues nothing, so it needs neither data pointers nor a device
     assert _call("rsq_subspace_correct", None, None, 1, 0, 4096, 4096, None, 32, None)[0] == 0

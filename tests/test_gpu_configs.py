@@ -202,6 +202,33 @@ def test_config4_w3a3_rank_sweep():
     assert all(b <= a + 2e-3 for a, b in zip(errs, errs[1:]))
 
 
+def test_dense_comparator_against_oracle():
+    """The dense alternative the benchmark times beside the correction (h T as a bf16
+    GEMM) reproduces the oracle's float64 h T; the rank-r correction's distance
+    from it equals the oracle's approximation error."""
+    import torch
+    rsq = lib()
+    cfg = synth.CONFIGS[4]
+    h = synth.residual(cfg, 512)
+    hd = to_dev(h, "bf16")
+    _, T, _ = oracle_basis_all(4, "A", 64)
+    dense_gpu = to_host(torch.matmul(hd, torch.from_numpy(T.astype(np.float32)).cuda().to(torch.bfloat16)))
+    rows = np.arange(0, 512, 7)
+    ref = np.asarray(h, np.float64)[rows] @ T
+    err_dense = rel_l2(dense_gpu[rows], ref)
+    print(f"  dense bf16 h T rel_l2 vs float64 oracle: {err_dense:.2e}", flush=True)
+    assert err_dense < 2e-2
+    r = cfg.r
+    U, M = site_for_rank(4, "A", r)
+    out = torch.empty_like(hd)
+    rsq.rsq_subspace_correct(hd, out, gpu_site(U, M), r)
+    torch.cuda.synchronize()
+    err_gpu = rel_l2(to_host(out)[rows], ref)
+    err_oracle = rel_l2(online.correct(h[rows], U, M, "f32"), ref)
+    print(f"  rank-{r} correction vs dense: GPU {err_gpu:.4f}, oracle {err_oracle:.4f}", flush=True)
+    assert abs(err_gpu - err_oracle) < 5e-3
+
+
 @pytest.mark.parametrize("name,N,K", [("qkv_gqa", 6144, 4096), ("gate_up", 28672, 4096), ("down", 4096, 14336)])
 def test_config4_w3a3_gemms_full_size(name, N, K):
     print(f"case config4 gemm {name}", flush=True)
@@ -223,3 +250,51 @@ def test_config5_site_full_batch():
 def test_config5_gemms_full_size(name, N, K):
     print(f"case config5 gemm {name}", flush=True)
     gemm_sampled(4, 4096, N, K, seed=N + K + 5)
+
+
+# ------------------------------------------------------- chained layer (config 2)
+def test_config2_layer_chained_stage_by_stage():
+    """A decoder layer with the residual stream carried through (sites A and B,
+    o_proj and down_proj added to the residual in the GEMM epilogue): every
+    stage checked on sampled tokens against the oracle fed the GPU's own inputs."""
+    import torch
+    from rotation_bit_post_amd.path import LayerPath
+    cfg = synth.CONFIGS[2]
+    n = 256
+    ua, ma, _ = oracle_site(2, "A", cfg.r)
+    ub, mb, _ = oracle_site(2, "B", cfg.r)
+    path = LayerPath.build(2, n=n, sites={"A": (ua, ma), "B": (ub, mb)})
+    for _, _, fn in path.stages(correction=True, chain=True):
+        fn()
+    torch.cuda.synchronize()
+    b, bits, lin = path.bufs, cfg.bits, path.linears
+    rows = np.array([0, 1, 77, 128, 200, 255])
+    take = lambda t: to_host(t[torch.from_numpy(rows).cuda()])  # noqa: E731
+    codes = lambda t, k: packing.unpack(t[torch.from_numpy(rows).cuda()].cpu().numpy(), k, bits)  # noqa: E731
+    wq = {name: packing.unpack(l.codes.cpu().numpy(), l.K, bits) for name, l in lin.items()}
+    ws = {name: l.scales.cpu().numpy() for name, l in lin.items()}
+    h = synth.residual(cfg, n)
+    D, F = cfg.D, cfg.F
+
+    def site_check(h_in, U, M, which):
+        hp = take(b[f"h_{which}"])
+        assert rel_l2(hp, online.correct(h_in, U, M, "bf16")) < 2e-2
+        q_ref, s_ref = online.quant_act(hp, bits, True, 1e-5)
+        assert code_mismatch_ok(codes(b[f"codes_{which}"], D), q_ref)[0]
+        assert np.all(np.abs(take(b[f"scales_{which}"]) - s_ref) <= 1e-6 * s_ref)
+        return hp
+
+    ha = site_check(h[rows], ua, ma, "A")
+    # h2 = h_A + o_proj(o_in): the GPU's own codes and scales, bit-exact
+    acc_o = online.gemm(codes(b["codes_o_in"], D), wq["o"])
+    h2_ref = online.dequant_add(acc_o, take(b["scales_o_in"]), ws["o"], ha, "bf16")
+    assert np.array_equal(take(b["h2"]), np.asarray(h2_ref, np.float64))
+    hb = site_check(take(b["h2"]), ub, mb, "B")
+    acc_d = online.gemm(codes(b["codes_down_in"], F), wq["down"])
+    h3_ref = online.dequant_add(acc_d, take(b["scales_down_in"]), ws["down"], hb, "bf16")
+    assert np.array_equal(take(b["h3"]), np.asarray(h3_ref, np.float64))
+    # the two projections that leave the residual stream
+    for name, which in (("qkv", "A"), ("gate_up", "B")):
+        acc = online.gemm(codes(b[f"codes_{which}"], D), wq[name])
+        y_ref = online.dequant(acc, take(b[f"scales_{which}"]), ws[name], "bf16")
+        assert np.array_equal(take(b[f"y_{name}"]), np.asarray(y_ref, np.float64))

@@ -259,6 +259,34 @@ def test_qgemm_large_tiles_with_ragged_edges(bits, n, N, K):
     assert np.array_equal(np.asarray(y_gpu, np.float64), np.asarray(online.dequant(acc_ref, sa[rows], sw[cols], "bf16"), np.float64))
 
 
+@pytest.mark.parametrize("bits,n,N,K,ydt,inplace", [
+    (4, 37, 96, 256, "bf16", False), (4, 300, 4096, 512, "bf16", True), (3, 70, 288, 1056, "f32", False),
+    (4, 1000, 12320, 1024, "bf16", True), (4, 5, 64, 64, "f32", True),
+])
+def test_qgemm_residual_matches_oracle(bits, n, N, K, ydt, inplace):
+    rsq = lib()
+    import torch
+    print(f"case qgemm-residual bits={bits} n={n} N={N} K={K} y={ydt} inplace={inplace}", flush=True)
+    rng = np.random.default_rng(n + N + K + 11)
+    qa, qw = _random_codes(n, K, bits, rng), _random_codes(N, K, bits, rng)
+    sa = rng.uniform(0.01, 2.0, n).astype(np.float32)
+    sw = rng.uniform(1e-3, 1e-2, N).astype(np.float32)
+    res = (rng.standard_normal((n, N)) * 3).astype(np.float32)
+    if ydt == "bf16":
+        res = round_to_bf16(res).astype(np.float32)
+    res_dev = to_dev(res, ydt)
+    a_dev = torch.from_numpy(packing.pack(qa, bits)).cuda()
+    w_dev = torch.from_numpy(packing.pack(qw, bits)).cuda()
+    y = res_dev if inplace else torch.empty_like(res_dev)
+    rsq.rsq_qgemm_residual(a_dev, to_dev(sa, "f32"), n, w_dev, to_dev(sw, "f32"), N, K, bits, res_dev, y)
+    torch.cuda.synchronize()
+    rows = np.unique(np.r_[0, n - 1, rng.choice(n, min(n, 48), replace=False)])
+    acc_ref = online.gemm(qa[rows], qw)
+    y_ref = online.dequant_add(acc_ref, sa[rows], sw, res[rows], ydt)
+    got = to_host(y[torch.from_numpy(rows).cuda()])
+    assert np.array_equal(np.asarray(got, np.float64), np.asarray(y_ref, np.float64))
+
+
 def test_qgemm_strided_output_and_minimum_codes():
     rsq = lib()
     import torch

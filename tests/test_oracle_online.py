@@ -323,3 +323,74 @@ def test_bf16_rounding_worked_values():
     m, e = np.frexp(r)
     assert np.array_equal(np.ldexp(m, 8), np.rint(np.ldexp(m, 8)))
     assert np.all(np.abs(r - x) <= np.ldexp(1.0, np.frexp(x)[1] - 9) * (1 + 1e-12))
+
+
+# ------------------------------------------------------------ residual add
+def test_dequant_add_with_zero_residual_is_dequant():
+    rng = np.random.default_rng(44)
+    acc = online.gemm(rng.integers(-7, 8, (5, 96)), rng.integers(-7, 8, (7, 96)))
+    sa = rng.uniform(0.01, 1, 5).astype(np.float32)
+    sw = rng.uniform(0.001, 0.01, 7).astype(np.float32)
+    for dt in ("f32", "bf16"):
+        assert np.array_equal(online.dequant_add(acc, sa, sw, np.zeros((5, 7), np.float32), dt),
+                              online.dequant(acc, sa, sw, dt))
+
+
+def test_dequant_add_with_zero_codes_returns_the_residual():
+    rng = np.random.default_rng(45)
+    r = round_to_bf16(rng.standard_normal((4, 32)) * 10)
+    y = online.dequant_add(np.zeros((4, 32), np.int64), np.ones(4, np.float32), np.ones(32, np.float32), r, "bf16")
+    assert np.array_equal(y, r)
+
+
+def test_dequant_add_within_three_roundings_of_the_exact_sum():
+    rng = np.random.default_rng(46)
+    acc = online.gemm(rng.integers(-7, 8, (6, 128)), rng.integers(-7, 8, (9, 128)))
+    sa = rng.uniform(0.01, 1, 6).astype(np.float32)
+    sw = rng.uniform(0.001, 0.01, 9).astype(np.float32)
+    r = rng.standard_normal((6, 9)).astype(np.float32)
+    y = online.dequant_add(acc, sa, sw, r, "f32").astype(np.float64)
+    v = acc * sa[:, None].astype(np.float64) * sw[None, :].astype(np.float64)
+    exact = v + r
+    # two roundings inside v (relative to |v|), one of the sum (relative to |y|)
+    ulp = lambda x: np.spacing(np.abs(x).astype(np.float32)).astype(np.float64)  # noqa: E731
+    assert np.all(np.abs(y - exact) <= 2 * ulp(v) + ulp(y))
+
+
+def _chain_inputs(d=64, f=96, n=6, seed=47):
+    rng = np.random.default_rng(seed)
+    h = round_to_bf16(rng.standard_normal((n, d)))
+    o_in = round_to_bf16(rng.standard_normal((n, d)))
+    down_in = round_to_bf16(rng.standard_normal((n, f)))
+
+    def lin(nout, k, zero=False):
+        w = np.zeros((nout, k), np.float32) if zero else (rng.standard_normal((nout, k)) * 0.05).astype(np.float32)
+        q, s = prep.quantize_weight(w, 4)
+        return packing.pack(q, 4), s
+    return h, o_in, down_in, lin
+
+
+def test_layer_chain_with_identity_sites_and_zero_outputs_keeps_the_residual():
+    d, f = 64, 96
+    h, o_in, down_in, lin = _chain_inputs(d, f)
+    u = np.linalg.qr(np.random.default_rng(48).standard_normal((d, 2)))[0].astype(np.float32)
+    site = (u, np.zeros((2, 2), np.float32))
+    weights = {"qkv": lin(3 * d, d), "o": lin(d, d, zero=True), "gate_up": lin(2 * f, d), "down": lin(d, f, zero=True)}
+    out = online.layer_chained(h, site, site, weights, o_in, down_in, "bf16", 4, 1e-5, "bf16")
+    assert np.array_equal(out["h2"], h) and np.array_equal(out["h3"], h)
+
+
+def test_layer_chain_carries_each_residual_add_into_the_next_site():
+    d, f = 64, 96
+    h, o_in, down_in, lin = _chain_inputs(d, f, seed=49)
+    u = np.linalg.qr(np.random.default_rng(50).standard_normal((d, 2)))[0].astype(np.float32)
+    site = (u, np.zeros((2, 2), np.float32))
+    weights = {"qkv": lin(3 * d, d), "o": lin(d, d), "gate_up": lin(2 * f, d), "down": lin(d, f)}
+    out = online.layer_chained(h, site, site, weights, o_in, down_in, "bf16", 4, 1e-5, "bf16")
+    # identity sites: h2 = bf16(h + o(o_in)), site B sees h2, h3 = bf16(h2 + down(down_in))
+    o_y = online.qgemm_packed(*online.quant_act_packed(o_in, 4, False)[:2], *weights["o"], d, 4, "f32")[0]
+    d_y = online.qgemm_packed(*online.quant_act_packed(down_in, 4, False)[:2], *weights["down"], f, 4, "f32")[0]
+    h2 = round_to_bf16(o_y.astype(np.float32) + h.astype(np.float32))
+    assert np.array_equal(out["h2"], h2)
+    assert np.array_equal(out["siteB"]["h_out"], h2)
+    assert np.array_equal(out["h3"], round_to_bf16(d_y.astype(np.float32) + h2.astype(np.float32)))
