@@ -21,6 +21,8 @@
 // token (l % 16) and columns 32c + 8(l / 16) .. +7 of chunk c: the B operand
 // of the projection (k-slot e = column 32c + 8g + e) and, by the row order
 // chosen for V, also the accumulator layout of the reprojection.
+#include <type_traits>
+
 #include "rsq_device.h"
 #include "rsq_internal.h"
 
@@ -106,6 +108,10 @@ template <> struct Row8<uint16_t> {  // bfloat16: 8 values in 16 bytes
         return static_cast<double>(s);
     }
     __device__ __forceinline__ void operands(v8bf &hi, v8bf &lo) const { hi = as_v8bf(raw); (void)lo; }
+    __device__ __forceinline__ void shuffle_xor(int mask) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) raw[q] = __shfl_xor(raw[q], mask, kWave);
+    }
     // Hide the value from common-subexpression elimination, so unpacked copies
     // are recomputed per phase instead of being kept live across phases.
     __device__ __forceinline__ void opaque() { asm volatile("" : "+v"(raw)); }
@@ -144,6 +150,13 @@ template <> struct Row8<float> {  // float32: 8 values in 32 bytes
         lo = as_v8bf(l);
     }
     __device__ __forceinline__ void opaque() { asm volatile("" : "+v"(a), "+v"(b)); }
+    __device__ __forceinline__ void shuffle_xor(int mask) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            a[q] = __shfl_xor(a[q], mask, kWave);
+            b[q] = __shfl_xor(b[q], mask, kWave);
+        }
+    }
     static constexpr bool kSplit = true;
 };
 
@@ -271,10 +284,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void correct_kernel(
     }
 
     // 4. reprojection + residual (C: 16 columns of d x 16 tokens, seeded with
-    //    h), rounded to the storage type; with QUANT also the RMSNorm
-    //    statistics of the rounded values
-    double ss = 0.0;
-    float am = 0.0f;
+    //    h), rounded to the storage type
 #pragma unroll
     for (int m = 0; m < CPW; ++m) {
         const int sl = m % PD;
@@ -292,14 +302,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void correct_kernel(
                 }
             }
             hr[m].set4(b, cacc);
-            if constexpr (QUANT) {
-                // rounding is monotone and odd: the largest rounded magnitude
-                // is the rounded largest magnitude
-#pragma unroll
-                for (int v = 0; v < 4; ++v) am = fmaxf(am, fabsf(cacc[v]));
-            }
         }
-        if constexpr (QUANT) ss += hr[m].sumsq();
         if (m + PD < CPW) {
             const int cn = w + nw * (m + PD);
 #pragma unroll
@@ -315,24 +318,41 @@ __global__ __launch_bounds__(64 * kMaxWaves) void correct_kernel(
 
 #pragma unroll
     for (int m = 0; m < CPW; ++m) hr[m].opaque();
-    if constexpr (QUANT) {
-        // 5. row statistics over the waves
+    // Statistics, scale, quantisation and packing of NC chunks per lane: chunk
+    // m of this lane is global chunk w + nw * (m + base) of token t0 + tok.
+    // PAIR: lanes l and l ^ 8 hold two halves of one token's chunks.
+    auto quant_epilogue = [&](auto nc_c, auto pair_c, int base, int tok) {
+        constexpr int NC = decltype(nc_c)::value;
+        constexpr bool PAIR = decltype(pair_c)::value;
+        const int64_t tt = t0 + tok;
+        const bool ok = tok < tb && tt < n;
+        double ss = 0.0;
+        float am = 0.0f;
+#pragma unroll
+        for (int m = 0; m < NC; ++m) {
+            ss += hr[m].sumsq();
+#pragma unroll
+            for (int e = 0; e < 8; ++e) am = fmaxf(am, fabsf(hr[m].get(e)));
+        }
+        if constexpr (PAIR) {
+            ss += shfl_xor_f64(ss, 8);
+            am = wave_max_xor(am, 8);
+        }
         ss += shfl_xor_f64(ss, 16);
         ss += shfl_xor_f64(ss, 32);
         am = wave_max_xor(am, 16);
         am = wave_max_xor(am, 32);
-        if (g == 0) {
-            lss[w * 16 + tl] = ss;
-            lam[w * 16 + tl] = am;
+        if (g == 0 && (!PAIR || tl < 8)) {
+            lss[w * 16 + tok] = ss;
+            lam[w * 16 + tok] = am;
         }
         __syncthreads();
         double tot = 0.0;
         float amax = 0.0f;
         for (int ww = 0; ww < nw; ++ww) {
-            tot += lss[ww * 16 + tl];
-            amax = fmaxf(amax, lam[ww * 16 + tl]);
+            tot += lss[ww * 16 + tok];
+            amax = fmaxf(amax, lam[ww * 16 + tok]);
         }
-        if constexpr (!SPLIT) amax = bf16_to_f32(f32_to_bf16(amax));
         const float inv = static_cast<float>(1.0 / sqrt(tot / static_cast<double>(d) + static_cast<double>(eps)));
         float mval;
         if (norm_w == nullptr) {
@@ -340,31 +360,30 @@ __global__ __launch_bounds__(64 * kMaxWaves) void correct_kernel(
         } else {
             float a2 = 0.0f;
 #pragma unroll
-            for (int m = 0; m < CPW; ++m) {
-                const float *wp = norm_w + 32 * (w + nw * m) + 8 * g;
+            for (int m = 0; m < NC; ++m) {
+                const float *wp = norm_w + 32 * (w + nw * (m + base)) + 8 * g;
                 const v4f w0 = *reinterpret_cast<const v4f *>(wp), w1 = *reinterpret_cast<const v4f *>(wp + 4);
 #pragma unroll
                 for (int e = 0; e < 8; ++e) a2 = fmaxf(a2, fabsf((hr[m].get(e) * inv) * (e < 4 ? w0[e] : w1[e - 4])));
             }
+            if constexpr (PAIR) a2 = wave_max_xor(a2, 8);
             a2 = wave_max_xor(a2, 16);
             a2 = wave_max_xor(a2, 32);
-            if (g == 0) lwm[w * 16 + tl] = a2;
+            if (g == 0 && (!PAIR || tl < 8)) lwm[w * 16 + tok] = a2;
             __syncthreads();
             mval = 0.0f;
-            for (int ww = 0; ww < nw; ++ww) mval = fmaxf(mval, lwm[ww * 16 + tl]);
+            for (int ww = 0; ww < nw; ++ww) mval = fmaxf(mval, lwm[ww * 16 + tok]);
         }
 #pragma unroll
-        for (int m = 0; m < CPW; ++m) hr[m].opaque();
+        for (int m = 0; m < NC; ++m) hr[m].opaque();
         const float *nw_q = norm_w;
         asm volatile("" : "+s"(nw_q));  // reload the weights below instead of keeping them live
         const int qmax = (1 << (bits - 1)) - 1;
         const float s = __fdiv_rn(mval, static_cast<float>(qmax));
         const float inv_s = s > 0.0f ? __fdiv_rn(1.0f, s) : 0.0f;
         const size_t rowb = bits == 4 ? static_cast<size_t>(d) / 2 : static_cast<size_t>(d) * 3 / 8;
-
-        // 6. quantise + pack (norm weights, if any, in a loop of their own)
         auto quant_chunk = [&](int m, const float *wts) {
-            const int c = w + nw * m;
+            const int c = w + nw * (m + base);
             uint32_t u[8];
             if (wts != nullptr) {
                 const v4f w0 = *reinterpret_cast<const v4f *>(wts + 32 * c + 8 * g);
@@ -379,37 +398,62 @@ __global__ __launch_bounds__(64 * kMaxWaves) void correct_kernel(
                 uint32_t word = 0;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) word |= (u[e] & 0xFu) << (4 * e);
-                if (valid) *reinterpret_cast<uint32_t *>(codes + t * rowb + 16 * c + 4 * g) = word;
+                if (ok) *reinterpret_cast<uint32_t *>(codes + tt * rowb + 16 * c + 4 * g) = word;
             } else {
                 uint32_t own, low[3];
                 int3_lane_parts(u, own, low);
-                const int src = 48 + tl;  // the g = 3 lane of this token
+                const int src = 48 + tl;  // the g = 3 lane of this token and chunk
                 const uint32_t l0 = __shfl(low[0], src, kWave), l1 = __shfl(low[1], src, kWave),
                                l2 = __shfl(low[2], src, kWave);
                 const uint32_t word = own | (g == 0 ? l0 : (g == 1 ? l1 : l2));
-                if (valid && g < 3) *reinterpret_cast<uint32_t *>(codes + t * rowb + 12 * c + 4 * g) = word;
+                if (ok && g < 3) *reinterpret_cast<uint32_t *>(codes + tt * rowb + 12 * c + 4 * g) = word;
             }
+            if (ok) hr[m].store(h_out + tt * ld_h + 32 * c + 8 * g);
         };
         if (nw_q != nullptr) {
 #pragma unroll
-            for (int m = 0; m < CPW; ++m) {
+            for (int m = 0; m < NC; ++m) {
                 quant_chunk(m, nw_q);
                 __builtin_amdgcn_sched_barrier(0);
             }
         } else {
 #pragma unroll
-            for (int m = 0; m < CPW; ++m) {
+            for (int m = 0; m < NC; ++m) {
                 quant_chunk(m, nullptr);
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
-        if (valid && w == 0 && g == 0) scales[t] = s;
+        if (ok && w == 0 && g == 0 && base == 0) scales[tt] = s;
+    };
+
+    if constexpr (QUANT) {
+        // 5-6. RMSNorm statistics, scale, quantisation and packing. With 8-token
+        // blocks the lanes of tokens 8-15 hold no token of their own: they take
+        // over the upper half of the chunks of token (l % 16) - 8, which halves
+        // the per-element work of every lane.
+        if constexpr (CPW >= 2 && CPW <= 16) {   // (32 chunks: registers are too tight for two variants)
+            if (tb <= 8) {
+#pragma unroll
+                for (int m = 0; m < CPW / 2; ++m) {
+                    Row8<T> up = hr[m + CPW / 2];
+                    up.shuffle_xor(8);
+                    if (tl >= 8) hr[m] = up;
+                }
+                quant_epilogue(std::integral_constant<int, CPW / 2>{}, std::true_type{}, tl >= 8 ? CPW / 2 : 0, tl & 7);
+            } else {
+                quant_epilogue(std::integral_constant<int, CPW>{}, std::false_type{}, 0, tl);
+            }
+        } else {
+            quant_epilogue(std::integral_constant<int, CPW>{}, std::false_type{}, 0, tl);
+        }
     }
 
-    // 7. h' -> HBM
-    if (valid) {
+    // 7. h' -> HBM (the quantising variant stores it in its epilogue)
+    if constexpr (!QUANT) {
+        if (valid) {
 #pragma unroll
-        for (int m = 0; m < CPW; ++m) hr[m].store(h_out + t * ld_h + 32 * (w + nw * m) + 8 * g);
+            for (int m = 0; m < CPW; ++m) hr[m].store(h_out + t * ld_h + 32 * (w + nw * m) + 8 * g);
+        }
     }
 }
 

@@ -326,9 +326,17 @@ hipError_t launch_t(const uint8_t *a, const float *sa, int64_t n, const uint8_t 
 template <int BITS, typename YT>
 hipError_t launch_b(const uint8_t *a, const float *sa, int64_t n, const uint8_t *w, const float *sw, int64_t N,
                     int64_t K, void *y, int64_t ld_y, int32_t *acc_out, const void *res, int64_t ld_r, hipStream_t s) {
-    if (n <= 32) return launch_t<BITS, 32, 128, 1, 4, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s);
-    if (n <= 64) return launch_t<BITS, 64, 128, 2, 2, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s);
     const int64_t cus = device_cus();
+    // small batches (decode) stream the weights once: narrow channel tiles give
+    // enough workgroups to keep every CU's memory pipeline busy
+    if (n <= 32) {
+        if ((N + 127) / 128 < 2 * cus) return launch_t<BITS, 32, 32, 1, 1, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s);
+        return launch_t<BITS, 32, 128, 1, 4, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s);
+    }
+    if (n <= 64) {
+        if ((N + 127) / 128 < 2 * cus) return launch_t<BITS, 64, 32, 2, 1, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s);
+        return launch_t<BITS, 64, 128, 2, 2, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s);
+    }
     const int64_t mt = (n + 255) / 256;
     const int64_t rounds_128 = (mt * ((N + 127) / 128) + cus - 1) / cus;
     const int64_t rounds_256 = (mt * ((N + 255) / 256) + cus - 1) / cus;
