@@ -233,6 +233,30 @@ class LayerPath:
         for _, _, fn in self.stages(correction, chain):
             fn()
 
+    def outputs(self, chain: bool = False):
+        """Every tensor a step writes (for comparing two ways of running it)."""
+        keys = [k for k in self.bufs if k.startswith(("h_", "codes_", "scales_", "y_")) or k in ("h2", "h3")]
+        if chain:   # the o / down results land on the residual stream instead
+            keys = [k for k in keys if k not in ("y_o", "y_down")]
+        else:
+            keys = [k for k in keys if k not in ("h2", "h3")]
+        return {k: self.bufs[k] for k in sorted(keys)}
+
+    def capture(self, correction: bool = True, chain: bool = False):
+        """One step recorded as a HIP graph (launches only: the step allocates
+        nothing and sets no memory), replayed with ``graph.replay()``."""
+        import torch
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            self.step(correction, chain)      # first launches of every kernel outside the capture
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            self.step(correction, chain)
+        return graph
+
     # -------------------------------------------------- algorithmic work
     def stage_work(self, name: str):
         """(algorithmic bytes, algorithmic integer ops) of one stage launch."""

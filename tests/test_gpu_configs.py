@@ -298,3 +298,30 @@ def test_config2_layer_chained_stage_by_stage():
         acc = online.gemm(codes(b[f"codes_{which}"], D), wq[name])
         y_ref = online.dequant(acc, take(b[f"scales_{which}"]), ws[name], "bf16")
         assert np.array_equal(take(b[f"y_{name}"]), np.asarray(y_ref, np.float64))
+
+
+def test_layer_step_replayed_as_a_hip_graph_matches_eager():
+    """The chained layer recorded once as a HIP graph: every replay, with eager
+    work and synchronisations in between, reproduces the eager step bit for bit."""
+    import torch
+    from rotation_bit_post_amd.path import LayerPath
+    rsq = lib()
+    cfg = synth.CONFIGS[2]
+    ua, ma, _ = oracle_site(2, "A", cfg.r)
+    ub, mb, _ = oracle_site(2, "B", cfg.r)
+    path = LayerPath.build(2, n=192, sites={"A": (ua, ma), "B": (ub, mb)})
+    path.step(chain=True)
+    torch.cuda.synchronize()
+    ref = {k: v.clone() for k, v in path.outputs(chain=True).items()}
+    graph = path.capture(chain=True)
+    scratch_c = empty_u8(192, cfg.D // 2)
+    scratch_s = empty_f32(192)
+    for rep in range(3):
+        for v in path.outputs(chain=True).values():
+            v.zero_()
+        rsq.rsq_quant_act(path.bufs["h"], scratch_c, scratch_s, cfg.bits, rmsnorm=True)   # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        bad = [k for k, v in path.outputs(chain=True).items() if not torch.equal(v, ref[k])]
+        assert not bad, (rep, bad)
