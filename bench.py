@@ -45,6 +45,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample", type=int, default=16, help="tokens in the CPU oracle sample")
     p.add_argument("--no-dense", action="store_true", help="skip the dense h T comparator")
+    p.add_argument("--prep", choices=("device", "host"), default="device",
+                   help="where the synthetic sites are prepared (offline step, not timed in the step)")
     p.add_argument("--rank-sweep", action="store_true",
                    help="only the correction at every rank of the workload (time and error against dense h T)")
     p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -218,7 +220,7 @@ def main():
 
     t_build = time.perf_counter()
     progress(f"building config {args.config} (sites, weights, inputs)")
-    base = LayerPath.build(args.config, keep_mismatch=not args.no_dense)
+    base = LayerPath.build(args.config, keep_mismatch=not args.no_dense, prep=args.prep)
     copies = [base] + [base.clone() for _ in range(args.copies - 1)]
     torch.cuda.synchronize()
     t_build = time.perf_counter() - t_build
@@ -395,6 +397,7 @@ def main():
             "note": "eager: the eight launches back to back; graph: the same launches recorded once as a HIP "
                     "graph and replayed (outputs checked bit-identical first); value uses the faster",
         },
+        "offline_prep": base.prep_info,
         "wall_s_timed": round(wall, 3),
         "setup_s": round(t_build, 1),
         "kernel_source_hash": src_hash,

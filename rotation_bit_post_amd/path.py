@@ -23,6 +23,8 @@ no norm); the sites come from ``offline.convert_site`` and rsq_site_prepare.
 """
 from __future__ import annotations
 
+import time
+
 from dataclasses import dataclass, field
 
 import numpy as np
@@ -104,15 +106,18 @@ class LayerPath:
     linears: dict = field(default_factory=dict)
     bufs: dict = field(default_factory=dict)
     mismatch: dict = field(default_factory=dict)   # site -> T (float32), kept on request
+    prep_info: dict = field(default_factory=dict)  # site -> how its (U_r, M) was prepared
 
     @classmethod
     def build(cls, cid: int, n: int | None = None, r: int | None = None, gqa: bool = True,
-              sites=None, weights=None, keep_mismatch: bool = False) -> "LayerPath":
+              sites=None, weights=None, keep_mismatch: bool = False, prep: str = "host") -> "LayerPath":
         """Device-resident inputs and outputs of one layer path.
 
         sites: optional {"A": (U, M), "B": (U, M)}; weights: optional
         {linear name: float32 (N, K)} - both default to the seeded synthetic ones.
         keep_mismatch: also keep each synthetic site's dense T (for comparisons).
+        prep: "host" (float64 eigensolver on the CPU) or "device" (float64
+        block subspace iteration on the GPU) for the synthetic sites.
         """
         cfg = CONFIGS[cid]
         self = cls(cfg, n or cfg.n, r or cfg.r, gqa)
@@ -122,9 +127,27 @@ class LayerPath:
             which = src[-1]
             if sites is not None:
                 U, M = sites[which]
+            elif prep == "device":
+                from . import offline_device as OD
+                t0 = time.perf_counter()
+                r_in = OD.synthetic_rotation_device(G.skew_generator(cfg, which, "in"), cfg.eps_rot)
+                r_out = OD.synthetic_rotation_device(G.skew_generator(cfg, which, "out"), cfg.eps_rot)
+                torch.cuda.synchronize()
+                t1 = time.perf_counter()
+                U, M, iters, res = OD.convert_site_device(r_in, r_out, self.r)
+                t2 = time.perf_counter()
+                if keep_mismatch:
+                    self.mismatch[which] = (r_out.T @ r_in).to(torch.float32).cpu().numpy()
+                self.prep_info[which] = {"where": "device", "rotations_s": round(t1 - t0, 3),
+                                         "subspace_s": round(t2 - t1, 3), "iterations": iters, "residual": res}
+                del r_in, r_out
             else:
+                t0 = time.perf_counter()
                 t = synthetic_mismatch(cfg, which)
+                t1 = time.perf_counter()
                 U, M = offline.convert_mismatch(t, self.r)
+                self.prep_info[which] = {"where": "host", "rotations_s": round(t1 - t0, 3),
+                                         "subspace_s": round(time.perf_counter() - t1, 3)}
                 if keep_mismatch:
                     self.mismatch[which] = t.astype(np.float32)
                 del t

@@ -325,3 +325,23 @@ def test_layer_step_replayed_as_a_hip_graph_matches_eager():
         torch.cuda.synchronize()
         bad = [k for k, v in path.outputs(chain=True).items() if not torch.equal(v, ref[k])]
         assert not bad, (rep, bad)
+
+
+def test_device_offline_prep_matches_oracle_at_full_size():
+    """Site A of the LLaMA-2-7B-shaped workload prepared on the GPU (float64 block
+    subspace iteration) spans the oracle's SVD subspace and acts as the same operator."""
+    import torch
+    from rotation_bit_post_amd import offline_device as OD
+    cfg = synth.CONFIGS[2]
+    print("case device prep config 2 site A", flush=True)
+    r_in = OD.synthetic_rotation_device(synth.skew_generator(cfg, "A", "in"), cfg.eps_rot)
+    r_out = OD.synthetic_rotation_device(synth.skew_generator(cfg, "A", "out"), cfg.eps_rot)
+    u, m, iters, res = OD.convert_site_device(r_in, r_out, cfg.r)
+    print(f"  {iters} iterations, residual {res:.2e}", flush=True)
+    assert res < 1e-9
+    uo, mo, _ = oracle_site(2, "A", cfg.r)
+    x = np.random.default_rng(5).standard_normal((16, cfg.D))
+    act = lambda uu, mm: x + ((x @ uu.astype(np.float64)) @ mm.astype(np.float64)) @ uu.astype(np.float64).T  # noqa: E731
+    assert rel_l2(act(u, m), act(uo, mo)) < 1e-5
+    cosines = np.linalg.svd(u.astype(np.float64).T @ uo.astype(np.float64), compute_uv=False)
+    assert cosines.min() > 1 - 1e-5          # every principal angle between the subspaces is ~0
