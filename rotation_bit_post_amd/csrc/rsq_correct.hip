@@ -165,11 +165,16 @@ __device__ __forceinline__ v8bf load_op(const uint16_t *p) { return as_v8bf(*rei
 
 // ------------------------------------------------------------ main kernel
 // T: uint16_t (bf16) or float. CPW: 32-column chunks per wave. R32: r_pad / 32.
-template <typename T, int CPW, int R32, bool QUANT>
+// COLS (small batches, no quantisation): CPW workgroups share a token block;
+// each forms the whole projection (U is read through L2 by all of them) but
+// reprojects and stores only its slice of nw chunks, one per wave, so a few
+// tokens still spread over many compute units.
+template <typename T, int CPW, int R32, bool QUANT, bool COLS = false>
 __global__ __launch_bounds__(64 * kMaxWaves) void correct_kernel(
     const T *__restrict__ h_in, T *__restrict__ h_out, int64_t n, int d, int64_t ld_h,
     const uint16_t *__restrict__ site, int tb, const float *__restrict__ norm_w, float eps, int bits,
     uint8_t *__restrict__ codes, float *__restrict__ scales) {
+    static_assert(!(COLS && QUANT), "the column-split variant does not quantise");
     constexpr bool SPLIT = Row8<T>::kSplit;
     constexpr int NJB = 2 * R32;               // 16-wide j blocks of the projection
     constexpr int RPS = 32 * R32 + 4;          // LDS row stride of the partial projections (floats)
@@ -190,7 +195,8 @@ __global__ __launch_bounds__(64 * kMaxWaves) void correct_kernel(
     const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
     const int lane = threadIdx.x & 63;
     const int g = lane >> 4, tl = lane & 15;
-    const int64_t t0 = static_cast<int64_t>(blockIdx.x) * tb;
+    const int slice = COLS ? static_cast<int>(blockIdx.x % CPW) : 0;
+    const int64_t t0 = static_cast<int64_t>(COLS ? blockIdx.x / CPW : blockIdx.x) * tb;
     const int64_t t = t0 + tl;
     const bool valid = tl < tb && t < n;
     // lanes without a token of their own read the block's first row (in
@@ -245,7 +251,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void correct_kernel(
     // first reprojection operands, in flight during the reduction below
     v8bf vh[PD][2][R32], vl[NL][2][R32];
 #pragma unroll
-    for (int p = 0; p < PD; ++p)
+    for (int p = 0; p < (COLS ? 0 : PD); ++p)
 #pragma unroll
         for (int b = 0; b < 2; ++b)
 #pragma unroll
@@ -281,6 +287,39 @@ __global__ __launch_bounds__(64 * kMaxWaves) void correct_kernel(
             }
             pl[kk] = as_v8bf(lo);
         }
+    }
+
+    if constexpr (COLS) {
+        // 4'. this workgroup's slice: chunk slice * nw + w for wave w, its
+        //     residual read again (an L2 hit: the projection just read it)
+        const int c = slice * nw + w;
+        Row8<T> hc;
+        hc.load(h_in + tload * ld_h + 32 * c + 8 * g);
+        v8bf vc[2][R32], vcl[2][R32];
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int kk = 0; kk < R32; ++kk) {
+                vc[b][kk] = load_op(v_hi + v_index(c, b, kk, lane, R32));
+                if constexpr (SPLIT) vcl[b][kk] = load_op(v_lo + v_index(c, b, kk, lane, R32));
+            }
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            v4f cacc;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) cacc[v] = hc.get(4 * b + v);
+#pragma unroll
+            for (int kk = 0; kk < R32; ++kk) {
+                cacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vc[b][kk], ph[kk], cacc, 0, 0, 0);
+                if constexpr (SPLIT) {
+                    cacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vcl[b][kk], ph[kk], cacc, 0, 0, 0);
+                    cacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vc[b][kk], pl[kk], cacc, 0, 0, 0);
+                }
+            }
+            hc.set4(b, cacc);
+        }
+        if (valid) hc.store(h_out + t * ld_h + 32 * c + 8 * g);
+        return;
     }
 
     // 4. reprojection + residual (C: 16 columns of d x 16 tokens, seeded with
@@ -460,10 +499,24 @@ __global__ __launch_bounds__(64 * kMaxWaves) void correct_kernel(
 template <typename T, int CPW, int R32, bool QUANT>
 hipError_t launch_t(const void *h_in, void *h_out, int64_t n, int d, int64_t ld_h, const void *site, int nw,
                     const float *norm_w, float eps, int bits, uint8_t *codes, float *scales, hipStream_t s) {
-    // 16 tokens per workgroup unless that leaves compute units idle
-    const int tb = (n + 15) / 16 >= device_cus() ? 16 : 8;
-    const unsigned blocks = static_cast<unsigned>((n + tb - 1) / tb);
-    hipLaunchKernelGGL((correct_kernel<T, CPW, R32, QUANT>), dim3(blocks), dim3(64 * nw), 0, s,
+    const int cus = device_cus();
+    const int tb = (n + 15) / 16 >= cus ? 16 : 8;
+    const int64_t blocks = (n + tb - 1) / tb;
+    // few tokens: split the columns over CPW workgroups per token block (not in
+    // place: other workgroups of the block still read the residual); the
+    // quantising call then normalises and quantises the stored rows
+    if constexpr (CPW >= 4) {
+        if (h_in != h_out && blocks * CPW <= cus) {
+            hipLaunchKernelGGL((correct_kernel<T, CPW, R32, false, true>), dim3(static_cast<unsigned>(blocks * CPW)),
+                               dim3(64 * nw), 0, s, static_cast<const T *>(h_in), static_cast<T *>(h_out), n, d, ld_h,
+                               static_cast<const uint16_t *>(site), tb, nullptr, 0.0f, bits, nullptr, nullptr);
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess || !QUANT) return e;
+            return launch_quant(h_out, sizeof(T) == 2 ? 1 : 0, n, d, ld_h, true, norm_w, eps, bits, codes, scales, s);
+        }
+    }
+    const unsigned grid = static_cast<unsigned>(blocks);
+    hipLaunchKernelGGL((correct_kernel<T, CPW, R32, QUANT>), dim3(grid), dim3(64 * nw), 0, s,
                        static_cast<const T *>(h_in), static_cast<T *>(h_out), n, d, ld_h,
                        static_cast<const uint16_t *>(site), tb, norm_w, eps, bits, codes, scales);
     return hipGetLastError();

@@ -65,24 +65,6 @@ __device__ __forceinline__ double shfl_xor_f64(double v, int mask) {
 }
 
 // ---------------------------------------------------- quantisation kernels
-// rint(a / s) with the float32 quotient rounded to nearest (ties to even),
-// computed as a * inv_s (inv_s = 1/s correctly rounded). The product is within
-// 2^-23 relative of a / s, so it can differ in rounding only when a / s is
-// within a few ulps of a half-integer; those rare cases take the exact division.
-__device__ __forceinline__ int quant_code(float a, float s, float inv_s, int qmax) {
-    float y = a * inv_s;
-    float ay = fabsf(y);
-    float frac = ay - floorf(ay);
-    float q;
-    if (fabsf(frac - 0.5f) < 4.0e-6f) {
-        q = rintf(__fdiv_rn(a, s));
-    } else {
-        q = rintf(y);
-    }
-    q = fminf(fmaxf(q, -static_cast<float>(qmax)), static_cast<float>(qmax));
-    return static_cast<int>(q);
-}
-
 // Code of a / s, for |a| <= qmax * s: the float32 quotient rounded to nearest,
 // then to the nearest integer (ties to even), as in rint(a / s). The quotient
 // starts as RN(a * inv_s) (inv_s = RN(1 / s)), within one ulp of a / s; one
@@ -114,38 +96,6 @@ __device__ __forceinline__ void int3_lane_parts(const uint32_t u[8], uint32_t &o
         low[0] |= (lo & 3u) << (8 * b);
         low[1] |= (hi & 3u) << (8 * b);
         low[2] |= ((lo >> 2) << (8 * b + 1)) | ((hi >> 2) << (8 * b));
-    }
-}
-
-// Pack 8 int4 codes (code e at nibble e) into one 32-bit word: byte j = c[2j] | c[2j+1] << 4.
-__device__ __forceinline__ uint32_t pack_int4x8(const int c[8]) {
-    uint32_t w = 0;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) w |= (static_cast<uint32_t>(c[e]) & 0xFu) << (4 * e);
-    return w;
-}
-
-// Contribution of 8 consecutive int3 codes (codes 8q..8q+7 of a 32-code group)
-// to the group's three words. OR-ing the contributions of q = 0..3 gives the group.
-__device__ __forceinline__ void int3_part(const int c[8], int q, uint32_t &w0, uint32_t &w1, uint32_t &w2) {
-    w0 = w1 = w2 = 0;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const uint32_t u = static_cast<uint32_t>(c[e]) & 7u;
-        const int slot = 2 * q + (e >> 2);
-        const int b = e & 3;
-        const int base = 8 * b;
-        if (slot < 6) {
-            const int shift = base + ((slot & 1) ? 2 : 5);
-            const uint32_t bits = u << shift;
-            if ((slot >> 1) == 0) w0 |= bits; else if ((slot >> 1) == 1) w1 |= bits; else w2 |= bits;
-        } else if (slot == 6) {
-            w0 |= (u & 3u) << base;
-            w2 |= ((u >> 2) & 1u) << (base + 1);
-        } else {
-            w1 |= (u & 3u) << base;
-            w2 |= ((u >> 2) & 1u) << base;
-        }
     }
 }
 
