@@ -216,6 +216,136 @@ struct GemmTile {
     }
 };
 
+// ---------------------------------------------------- decode-size batches
+// One lane's packed codes of one 128-code k step of one row: lane half h takes
+// codes [64h, 64h + 64) (groups 2h and 2h + 1) and matrix-core step s uses its
+// 16-code block s. Activations and weights use the same order, so the dot
+// products do not depend on it.
+template <int BITS> struct Frag;
+template <> struct Frag<4> {
+    v4u x0, x1;
+    __device__ __forceinline__ void load2(const uint8_t *g0, const uint8_t *g1) {
+        x0 = *reinterpret_cast<const v4u *>(g0);
+        x1 = *reinterpret_cast<const v4u *>(g1);
+    }
+    __device__ __forceinline__ v4i op(int s) const {
+        return s == 0 ? unpack_int4x16(x0[0], x0[1])
+                      : (s == 1 ? unpack_int4x16(x0[2], x0[3])
+                                : (s == 2 ? unpack_int4x16(x1[0], x1[1]) : unpack_int4x16(x1[2], x1[3])));
+    }
+};
+template <> struct Frag<3> {
+    uint32_t w[6];
+    __device__ __forceinline__ void load2(const uint8_t *g0, const uint8_t *g1) {  // 4-byte aligned
+        const uint32_t *q0 = reinterpret_cast<const uint32_t *>(g0);
+        const uint32_t *q1 = reinterpret_cast<const uint32_t *>(g1);
+        w[0] = q0[0]; w[1] = q0[1]; w[2] = q0[2];
+        w[3] = q1[0]; w[4] = q1[1]; w[5] = q1[2];
+    }
+    __device__ __forceinline__ v4i op(int s) const {
+        const int g = s >> 1;
+        return unpack_int3_half(w[3 * g], w[3 * g + 1], w[3 * g + 2], s & 1);
+    }
+};
+
+// n <= 64 tokens: the weights are streamed once, so what counts is how many
+// weight bytes are in flight. A workgroup owns 32 output channels and all
+// tokens (TM fragments of 32); its NW waves split the k steps (wave w takes
+// steps w, w + NW, ...), load their operands straight from global memory into
+// registers in the matrix-core layout two steps ahead, and sum their partial
+// accumulators through LDS at the end. No barrier inside the k loop.
+template <int BITS, int TM, int NW, typename YT>
+__global__ __launch_bounds__(NW * 64) void qgemv_kernel(const uint8_t *__restrict__ A, const float *__restrict__ sa,
+                                                        int n, const uint8_t *__restrict__ W,
+                                                        const float *__restrict__ sw, int N, int K,
+                                                        YT *__restrict__ y, int64_t ld_y,
+                                                        int32_t *__restrict__ acc_out, const YT *__restrict__ res,
+                                                        int64_t ld_r) {
+    using F = Fmt<BITS>;
+    constexpr int KSTEP_B = kBK * BITS / 8;   // packed bytes of one k step of a row
+    __shared__ int32_t red[NW][TM][16][64];
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+    const int h = lane >> 5, l32 = lane & 31;
+    const int bn0 = blockIdx.x * 32;
+    const uint32_t rb = static_cast<uint32_t>(K) * BITS / 8;
+    const int nkt = (K + kBK - 1) / kBK;
+    const uint8_t *wrow = W + static_cast<size_t>(min(bn0 + l32, N - 1)) * rb;
+    const uint8_t *arow[TM];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) arow[i] = A + static_cast<size_t>(min(32 * i + l32, n - 1)) * rb;
+
+    Frag<BITS> fa[2][TM], fw[2];
+    // groups past the row end read the row's first group (in bounds); the
+    // weight operand of such a group is zeroed before use
+    auto load_step = [&](int kt, int slot) {
+        kt = min(kt, nkt - 1);
+        const int k0 = kt * kBK + 64 * h;
+        const uint32_t off0 = k0 < K ? static_cast<uint32_t>(kt) * KSTEP_B + h * (KSTEP_B / 2) : 0u;
+        const uint32_t off1 = k0 + 32 < K ? static_cast<uint32_t>(kt) * KSTEP_B + h * (KSTEP_B / 2) + F::kGroupB : 0u;
+        fw[slot].load2(wrow + off0, wrow + off1);
+#pragma unroll
+        for (int i = 0; i < TM; ++i) fa[slot][i].load2(arow[i] + off0, arow[i] + off1);
+    };
+    v16i acc[TM];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][v] = 0;
+    auto compute = [&](int kt, int slot) {
+        if (kt >= nkt) return;
+#pragma unroll
+        for (int s = 0; s < kBK / 32; ++s) {
+            v4i wo = fw[slot].op(s);
+            if (kt * kBK + 64 * h + 32 * (s >> 1) >= K) wo = v4i{0, 0, 0, 0};
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+                acc[i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[slot][i].op(s), wo, acc[i], 0, 0, 0);
+        }
+    };
+    load_step(w, 0);
+    load_step(w + NW, 1);
+    for (int kt = w; kt < nkt; kt += 2 * NW) {
+        compute(kt, 0);
+        load_step(kt + 2 * NW, 0);
+        compute(kt + NW, 1);
+        load_step(kt + 3 * NW, 1);
+    }
+
+    // sum the waves' partial accumulators (fixed order) and write the outputs
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) red[w][i][v][lane] = acc[i][v];
+    __syncthreads();
+    for (int e = threadIdx.x; e < TM * 16 * 64; e += NW * 64) {
+        const int i = e / 1024, v = (e / 64) % 16, ln = e % 64;
+        int a = 0;
+#pragma unroll
+        for (int ww = 0; ww < NW; ++ww) a += red[ww][i][v][ln];
+        const int tok = 32 * i + 8 * (v >> 2) + 4 * (ln >> 5) + (v & 3);
+        const int ch = bn0 + (ln & 31);
+        if (tok < n && ch < N) {
+            a >>= F::kShift;
+            float val = (static_cast<float>(a) * sa[tok]) * sw[ch];
+            if (res != nullptr) val += from_out(res[static_cast<int64_t>(tok) * ld_r + ch]);
+            y[static_cast<int64_t>(tok) * ld_y + ch] = to_out<YT>(val);
+            if (acc_out != nullptr) acc_out[static_cast<int64_t>(tok) * N + ch] = a;
+        }
+    }
+}
+
+template <int BITS, int TM, typename YT>
+hipError_t launch_gemv(const uint8_t *a, const float *sa, int64_t n, const uint8_t *w, const float *sw, int64_t N,
+                       int64_t K, void *y, int64_t ld_y, int32_t *acc_out, const void *res, int64_t ld_r,
+                       hipStream_t s) {
+    constexpr int NW = 8;
+    hipLaunchKernelGGL((qgemv_kernel<BITS, TM, NW, YT>), dim3(static_cast<unsigned>((N + 31) / 32)), dim3(NW * 64), 0,
+                       s, a, sa, static_cast<int>(n), w, sw, static_cast<int>(N), static_cast<int>(K),
+                       static_cast<YT *>(y), ld_y, acc_out, static_cast<const YT *>(res), ld_r);
+    return hipGetLastError();
+}
+
 template <int BITS, int BM, int BN, int WM, int WN, int P, typename YT>
 __global__ __launch_bounds__(WM * WN * 64) void qgemm_kernel(const uint8_t *__restrict__ A,
                                                              const float *__restrict__ sa, int n,
@@ -327,15 +457,17 @@ template <int BITS, typename YT>
 hipError_t launch_b(const uint8_t *a, const float *sa, int64_t n, const uint8_t *w, const float *sw, int64_t N,
                     int64_t K, void *y, int64_t ld_y, int32_t *acc_out, const void *res, int64_t ld_r, hipStream_t s) {
     const int64_t cus = device_cus();
-    // small batches (decode) stream the weights once: narrow channel tiles give
-    // enough workgroups to keep every CU's memory pipeline busy
+    // decode-size batches stream the weights once: qgemv_kernel while its
+    // workgroups fit the CUs in one round (measured: faster for N = 4096 at 64
+    // tokens, slower for N = 12288 and 22016), else narrow channel tiles
+    const int64_t gemv_wgs = (N + 31) / 32;
     if (n <= 32) {
-        if ((N + 127) / 128 < 2 * cus) return launch_t<BITS, 32, 32, 1, 1, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s);
-        return launch_t<BITS, 32, 128, 1, 4, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s);
+        if (gemv_wgs <= 2 * cus) return launch_gemv<BITS, 1, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s);
+        return launch_t<BITS, 32, 32, 1, 1, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s);
     }
     if (n <= 64) {
-        if ((N + 127) / 128 < 2 * cus) return launch_t<BITS, 64, 32, 2, 1, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s);
-        return launch_t<BITS, 64, 128, 2, 2, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s);
+        if (gemv_wgs <= cus) return launch_gemv<BITS, 2, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s);
+        return launch_t<BITS, 64, 32, 2, 1, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s);
     }
     const int64_t mt = (n + 255) / 256;
     const int64_t rounds_128 = (mt * ((N + 127) / 128) + cus - 1) / cus;

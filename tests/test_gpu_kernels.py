@@ -189,7 +189,7 @@ def test_fused_correct_quant_equals_unfused_and_oracle():
 GEMM_CASES = [  # bits, n, N, K, y dtype
     (4, 1, 32, 32, "f32"), (4, 5, 96, 96, "bf16"), (3, 7, 64, 224, "f32"), (4, 64, 256, 256, "bf16"),
     (3, 65, 288, 4096, "bf16"), (4, 130, 256, 4096, "f32"), (4, 33, 512, 11008, "bf16"), (3, 200, 160, 1056, "f32"),
-    (4, 300, 4096, 512, "bf16"),
+    (4, 300, 4096, 512, "bf16"), (4, 20, 16448, 256, "bf16"), (3, 50, 8224, 224, "f32"),
 ]
 
 
