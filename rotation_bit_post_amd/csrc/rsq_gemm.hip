@@ -4,8 +4,9 @@
 //   y[t, j]   = (float(acc) * s_a[t]) * s_w[j]
 //
 // Packed tiles are loaded from HBM/L2, widened to int8 once per workgroup on
-// their way into LDS (double buffered, one barrier per 128-code k step) and
-// read back with 16-byte LDS loads straight into v_mfma_i32_32x32x32_i8.
+// their way into LDS (double buffered, one barrier per 128-code k step, placed
+// so that the multiplies of the step's last 32 codes run across it) and read
+// back with 16-byte LDS loads straight into v_mfma_i32_32x32x32_i8.
 // Widening only moves each code's bits to the top of its byte, so the matrix core multiplies 16*a by 16*w (int4) or 32*a by
 // 32*w (int3); the epilogue shifts the exact accumulator back. With codes in
 // [-7, 7] and K <= 28672 the scaled sum stays below 2^29. The k order inside
@@ -23,6 +24,7 @@ namespace rsq {
 namespace {
 
 constexpr int kBK = 128;       // codes per k step (4 matrix-core steps of 32)
+static_assert(kBK == 128, "the k step is written as four 32-code steps");
 constexpr int kRowLds = 144;   // LDS bytes per row: 128 int8 + 16 pad (conflict-free 16-byte reads)
 
 template <int BITS> struct Fmt;
@@ -158,13 +160,14 @@ struct GemmTile {
                 }
             }
         };
-        auto store_tile = [&](int kt, int buf, Group<BITS> *st) {
+        // widen groups [i0, i1) of a slot and write them to an LDS buffer
+        auto store_part = [&](int kt, uint8_t *buf, Group<BITS> *st, int i0, int i1) {
 #pragma unroll
-            for (int i = 0; i < GPT; ++i) {
+            for (int i = i0; i < i1; ++i) {
                 if constexpr (!FAST) st[i].keep_if(gvalid[i] && kt * kBK + gk[i] < K);
                 v4i lo, hi;
                 st[i].widen(lo, hi);
-                v4i *dst = reinterpret_cast<v4i *>(lds + buf * (LDS_BYTES / 2) + ldst[i]);
+                v4i *dst = reinterpret_cast<v4i *>(buf + ldst[i]);
                 dst[0] = lo;
                 dst[1] = hi;
             }
@@ -181,30 +184,57 @@ struct GemmTile {
 #pragma unroll
             for (int j = 0; j < TN; ++j) wo[slot][j] = *reinterpret_cast<const v4i *>(lb + wrow + 32 * j * kRowLds + 32 * s);
         };
-        // one k step: refill slot u with step kt + P, multiply step kt from
-        // LDS, then write step kt + 1 (slot u + 1) to the other LDS buffer
-        auto step = [&](int kt, int u) {
-            load_tile(kt + P, stage[u]);
-            __builtin_amdgcn_sched_barrier(0);  // issue the loads before this step's work
-            const uint8_t *lb = lds + (kt & 1) * (LDS_BYTES / 2);
-            read_ops(lb, 0, 0);
+        auto mfma = [&](int slot) {
 #pragma unroll
-            for (int s = 0; s < kBK / 32; ++s) {
-                if (s + 1 < kBK / 32) read_ops(lb, s + 1, (s + 1) & 1);
+            for (int i = 0; i < TM; ++i)
 #pragma unroll
-                for (int i = 0; i < TM; ++i)
+                for (int j = 0; j < TN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ao[slot][i], wo[slot][j], acc[i][j], 0, 0, 0);
+        };
+        // issue order inside one 32-code step: multiplies alternate with the
+        // LDS reads of the next step's operands
+        auto interleave = [&]() {
 #pragma unroll
-                    for (int j = 0; j < TN; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ao[s & 1][i], wo[s & 1][j], acc[i][j], 0, 0, 0);
+            for (int q = 0; q < TM + TN; ++q) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one matrix-core op
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
             }
-            store_tile(kt + 1, (kt + 1) & 1, stage[(u + 1) % P]);
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        // One k step. LDS buffer kt & 1 holds step kt and the operands of its
+        // first 32-code step are in slot 0. Slot u of the register ring is
+        // refilled with step kt + P; step kt + 1 (slot u + 1) is widened into
+        // the other buffer during the second and third 32-code steps. The
+        // barrier comes before the last 32-code step, so its multiplies cover
+        // the barrier and the LDS reads of step kt + 1's first operands.
+        // Buffer reuse: the other buffer was last read before the previous
+        // step's barrier, and this buffer is read only before this barrier.
+        auto step = [&](int kt, int u) {
+            const uint8_t *lb = lds + (kt & 1) * (LDS_BYTES / 2);
+            uint8_t *nb = lds + ((kt + 1) & 1) * (LDS_BYTES / 2);
+            load_tile(kt + P, stage[u]);
+            read_ops(lb, 1, 1);
+            mfma(0);
+            interleave();
+            read_ops(lb, 2, 0);
+            store_part(kt + 1, nb, stage[(u + 1) % P], 0, GPT / 2);
+            mfma(1);
+            interleave();
+            read_ops(lb, 3, 1);
+            store_part(kt + 1, nb, stage[(u + 1) % P], GPT / 2, GPT);
+            mfma(0);
+            interleave();
             __syncthreads();
+            read_ops(nb, 0, 0);
+            mfma(1);
+            interleave();
         };
 
 #pragma unroll
         for (int u = 0; u < P; ++u) load_tile(u, stage[u]);
-        store_tile(0, 0, stage[0]);
+        store_part(0, lds, stage[0], 0, GPT);
         __syncthreads();
+        read_ops(lds, 0, 0);
         int kt = 0;
         for (; kt + P <= nkt; kt += P) {
 #pragma unroll
