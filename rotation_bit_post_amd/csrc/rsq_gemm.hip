@@ -478,11 +478,11 @@ hipError_t launch_t(const uint8_t *a, const float *sa, int64_t n, const uint8_t 
     return hipGetLastError();
 }
 
-// Tile shape by problem size (measured on MI355X): 256 x 128 tiles with 8
-// waves on the layer shapes, 256 x 256 when the smaller tile would need
-// clearly more rounds of workgroups over the compute units (a 256 x 256 tile
-// does twice the work at about 10 % better efficiency); smaller tiles keep
-// small batches spread over the CUs.
+// Tile shape by problem size (measured on MI355X): 256 tokens x 128, 192 or
+// 256 channels with 8 waves on the layer shapes, whichever needs the least
+// time in whole rounds of workgroups over the compute units (wider tiles read
+// fewer LDS bytes per multiply); 128 x 128 for mid-size batches; narrow or
+// k-split kernels for decode-size batches.
 template <int BITS, typename YT>
 hipError_t launch_b(const uint8_t *a, const float *sa, int64_t n, const uint8_t *w, const float *sw, int64_t N,
                     int64_t K, void *y, int64_t ld_y, int32_t *acc_out, const void *res, int64_t ld_r, hipStream_t s) {
@@ -500,13 +500,21 @@ hipError_t launch_b(const uint8_t *a, const float *sa, int64_t n, const uint8_t 
         return launch_t<BITS, 64, 32, 2, 1, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s);
     }
     const int64_t mt = (n + 255) / 256;
-    const int64_t rounds_128 = (mt * ((N + 127) / 128) + cus - 1) / cus;
-    const int64_t rounds_256 = (mt * ((N + 255) / 256) + cus - 1) / cus;
-    if (n >= 256 && 18 * rounds_256 < 10 * rounds_128)
+    if (n < 256 || mt * ((N + 127) / 128) < 200)
+        return launch_t<BITS, 128, 128, 2, 2, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s);
+    // 256-token tiles, 128, 192 or 256 channels wide: rounds of workgroups
+    // over the CUs times the tile's relative time (tile width over its
+    // measured relative efficiency 1 : 1.09 : 1.17)
+    auto cost = [&](int64_t bn, int64_t eff100) {
+        const int64_t rounds = (mt * ((N + bn - 1) / bn) + cus - 1) / cus;
+        return rounds * bn * 100 * 117 / eff100;
+    };
+    const int64_t c128 = cost(128, 100), c192 = cost(192, 109), c256 = cost(256, 117);
+    if (c256 < c128 && c256 <= c192)
         return launch_t<BITS, 256, 256, 4, 2, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s);
-    if (n >= 256 && mt * ((N + 127) / 128) >= 200)
-        return launch_t<BITS, 256, 128, 4, 2, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s);
-    return launch_t<BITS, 128, 128, 2, 2, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s);
+    if (c192 < c128)
+        return launch_t<BITS, 256, 192, 4, 2, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s);
+    return launch_t<BITS, 256, 128, 4, 2, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s);
 }
 
 }  // namespace
