@@ -43,7 +43,7 @@ def parse():
     p.add_argument("--config", type=int, default=2)
     p.add_argument("--copies", type=int, default=2)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-sample", type=int, default=16, help="tokens in the CPU oracle sample")
+    p.add_argument("--cpu-sample", type=int, default=128, help="tokens in the CPU oracle sample (about 10 s on 16 cores)")
     p.add_argument("--no-dense", action="store_true", help="skip the dense h T comparator")
     p.add_argument("--prep", choices=("device", "host"), default="device",
                    help="where the synthetic sites are prepared (offline step, not timed in the step)")
@@ -294,6 +294,10 @@ def main():
             ev[i][j + 1].record(stream)
     torch.cuda.synchronize()
     stage_ms = {nm: [ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(args.steps)] for j, nm in enumerate(names)}
+    step_ms = sorted(ev[i][0].elapsed_time(ev[i][-1]) for i in range(args.steps))
+
+    def pct(q):
+        return round(step_ms[min(len(step_ms) - 1, int(q * (len(step_ms) - 1) + 0.5))], 5)
 
     progress("timed region done; correction-off pass")
     # correction off: each site only normalises and quantises (one global rotation, T = I)
@@ -394,8 +398,10 @@ def main():
             "ms_per_step_graph": None if ms_graph is None else round(ms_graph, 5),
             "graph_outputs_identical": graph_ok,
             "value_from": "graph" if ms_per_step != ms_eager else "eager",
+            "step_ms_p10_p50_p90": [pct(0.1), pct(0.5), pct(0.9)],
             "note": "eager: the eight launches back to back; graph: the same launches recorded once as a HIP "
-                    "graph and replayed (outputs checked bit-identical first); value uses the faster",
+                    "graph and replayed (outputs checked bit-identical first); value uses the faster; "
+                    "percentiles: single steps of the per-stage pass (events between stages add a little)",
         },
         "offline_prep": base.prep_info,
         "wall_s_timed": round(wall, 3),
