@@ -413,12 +413,35 @@ __global__ __launch_bounds__(WM * WN * 64) void qgemm_kernel(const uint8_t *__re
 
     // epilogue: lane holds channel l32 of each fragment and tokens 8(v/4) + 4h + v%4
     constexpr int OS = BN + 8;  // bf16 row stride of the output tile in LDS
+    constexpr int CPR = BN / 8;  // 16-byte chunks per row of the tile
     const bool staged = sizeof(YT) == 2 && acc_out == nullptr && ld_y % 8 == 0 &&
-                        (reinterpret_cast<uintptr_t>(y) & 15) == 0 && BM * OS * 2 <= T::LDS_BYTES;
+                        (reinterpret_cast<uintptr_t>(y) & 15) == 0 && BM * OS * 2 <= T::LDS_BYTES &&
+                        (res == nullptr || (ld_r % 8 == 0 && (reinterpret_cast<uintptr_t>(res) & 15) == 0));
     if (staged) {
         // bf16 tile through LDS, then 16-byte row-contiguous stores
         uint16_t *ot = reinterpret_cast<uint16_t *>(lds);
+        // the scales of this lane's 16 * TM tokens, loaded once for all its channels
+        float sat[TM][16];
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int tl = wm * (BM / WM) + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
+                sat[i][v] = bm0 + tl < n ? sa[bm0 + tl] : 0.0f;
+            }
         __syncthreads();  // every wave is done with the operand tiles
+        if (res != nullptr) {
+            // the residual tile, read with the same 16-byte row-contiguous
+            // accesses into the slots its sums will take (in place: this tile
+            // is read entirely before any of it is written)
+            for (int c = threadIdx.x; c < BM * CPR; c += WM * WN * 64) {
+                const int r = c / CPR, q = c % CPR;
+                if (bm0 + r < n && bn0 + 8 * q < N)
+                    *reinterpret_cast<v4u *>(ot + r * OS + 8 * q) =
+                        *reinterpret_cast<const v4u *>(res + static_cast<int64_t>(bm0 + r) * ld_r + bn0 + 8 * q);
+            }
+            __syncthreads();
+        }
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
             const int cl = wn * (BN / WN) + 32 * j + l32;
@@ -428,16 +451,13 @@ __global__ __launch_bounds__(WM * WN * 64) void qgemm_kernel(const uint8_t *__re
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
                     const int tl = wm * (BM / WM) + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
-                    const bool in = bm0 + tl < n && bn0 + cl < N;
-                    const float sat = bm0 + tl < n ? sa[bm0 + tl] : 0.0f;
-                    float val = (static_cast<float>(acc[i][j][v] >> F::kShift) * sat) * swj;
-                    if (res != nullptr && in) val += from_out(res[static_cast<int64_t>(bm0 + tl) * ld_r + bn0 + cl]);
+                    float val = (static_cast<float>(acc[i][j][v] >> F::kShift) * sat[i][v]) * swj;
+                    if (res != nullptr) val += bf16_to_f32(ot[tl * OS + cl]);
                     ot[tl * OS + cl] = to_out<uint16_t>(val);
                 }
             }
         }
         __syncthreads();
-        constexpr int CPR = BN / 8;  // 16-byte chunks per row
         for (int c = threadIdx.x; c < BM * CPR; c += WM * WN * 64) {
             const int r = c / CPR, q = c % CPR;
             if (bm0 + r < n && bn0 + 8 * q < N)
