@@ -30,7 +30,10 @@
  *              slot 6: u bits 0-1 -> bits 0-1 of lane b of w0, u bit 2 -> bit 1 of lane b of w2;
  *              slot 7: u bits 0-1 -> bits 0-1 of lane b of w1, u bit 2 -> bit 0 of lane b of w2.
  *  - Sizes: d and k multiples of 32; n_out a multiple of 32; n >= 0 (n = 0
- *    enqueues nothing); 1 <= r <= 64; bits 3 or 4.
+ *    enqueues nothing); 1 <= r <= 64; bits 3 or 4. Upper limits (beyond
+ *    them RSQ_ERR_UNSUPPORTED): k <= 65536 for the GEMMs (the int32
+ *    accumulator bound), k <= 32768 for rsq_quant_act (one row in the
+ *    registers of at most four waves), d <= 65536 for the correction.
  */
 #ifndef RSQ_H
 #define RSQ_H
@@ -46,7 +49,7 @@ typedef enum {
     RSQ_OK = 0,
     RSQ_ERR_INVALID_ARG = 1,   /* null pointer, negative or inconsistent size, misalignment */
     RSQ_ERR_UNSUPPORTED = 2,   /* valid but outside what the kernels handle (e.g. r > 64) */
-    RSQ_ERR_WORKSPACE = 3,     /* workspace missing or smaller than the size query says */
+    RSQ_ERR_WORKSPACE = 3,     /* reserved: no entry point takes a workspace */
     RSQ_ERR_HIP = 4            /* the HIP runtime refused a launch or a query */
 } rsq_status;
 

@@ -7,15 +7,17 @@
 // their way into LDS (double buffered, one barrier per 128-code k step, placed
 // so that the multiplies of the step's last 32 codes run across it) and read
 // back with 16-byte LDS loads straight into v_mfma_i32_32x32x32_i8.
-// Widening only moves each code's bits to the top of its byte, so the matrix core multiplies 16*a by 16*w (int4) or 32*a by
-// 32*w (int3); the epilogue shifts the exact accumulator back. With codes in
-// [-7, 7] and K <= 28672 the scaled sum stays below 2^29. The k order inside
-// a 32-code step is permuted the same way for both operands, which leaves the
-// dot products unchanged.
+// Widening only moves each code's bits to the top of its byte, so the matrix
+// core multiplies 16*a by 16*w (int4) or 32*a by 32*w (int3); the epilogue
+// shifts the exact accumulator back. Every widened code lies in [-128, 112],
+// so a product is at most 2^14 in magnitude and with K <= 65536 (checked at
+// the boundary) the scaled sum stays below 2^30. The k order inside a 32-code
+// step is permuted the same way for both operands, which leaves the dot
+// products unchanged.
 //
 // Matrix-core roles: A = activations (rows = tokens), B = weights (columns =
-// output channels), so each store instruction writes 32 consecutive channels
-// of a token row.
+// output channels). The epilogue stages the bf16 tile in LDS and writes it
+// with 16-byte row-contiguous stores.
 #include "rsq_device.h"
 #include "rsq_internal.h"
 
