@@ -367,6 +367,104 @@ __global__ __launch_bounds__(NW * 64) void qgemv_kernel(const uint8_t *__restric
     }
 }
 
+// n <= 64 tokens, 16 output channels per workgroup on v_mfma_i32_16x16x64_i8
+// (A = activations, rows = tokens; B = weights, columns = channels). A
+// 256-code k step is split over the lane quarters: lane quarter q takes codes
+// [64q, 64q + 64) (groups 2q and 2q + 1) and matrix-core step s its 16-code
+// block s, the same order for both operands. NW waves take k steps w, w + NW,
+// ... with operands loaded straight into registers two steps ahead and sum
+// their accumulators through LDS at the end in a fixed order.
+template <int BITS, int TB, int NW, typename YT>
+__global__ __launch_bounds__(NW * 64) void qgemv16_kernel(const uint8_t *__restrict__ A, const float *__restrict__ sa,
+                                                          int n, const uint8_t *__restrict__ W,
+                                                          const float *__restrict__ sw, int N, int K,
+                                                          YT *__restrict__ y, int64_t ld_y,
+                                                          int32_t *__restrict__ acc_out, const YT *__restrict__ res,
+                                                          int64_t ld_r) {
+    using F = Fmt<BITS>;
+    constexpr int KSB = 256 * BITS / 8;     // packed bytes of one 256-code step of a row
+    __shared__ int32_t red[NW][TB][4][64];
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+    const int q = lane >> 4, c16 = lane & 15;
+    const int bn0 = blockIdx.x * 16;
+    const uint32_t rb = static_cast<uint32_t>(K) * BITS / 8;
+    const int nkt = (K + 255) / 256;
+    const uint8_t *wrow = W + static_cast<size_t>(bn0 + c16) * rb;
+    const uint8_t *arow[TB];
+#pragma unroll
+    for (int i = 0; i < TB; ++i) arow[i] = A + static_cast<size_t>(min(16 * i + c16, n - 1)) * rb;
+
+    Frag<BITS> fa[2][TB], fw[2];
+    // groups past the row end read the row's first group (in bounds); the
+    // weight operand of such a group is zeroed before use
+    auto load_step = [&](int kt, int slot) {
+        kt = min(kt, nkt - 1);
+        const int k0 = kt * 256 + 64 * q;
+        const uint32_t base = static_cast<uint32_t>(kt) * KSB + q * (KSB / 4);
+        const uint32_t off0 = k0 < K ? base : 0u;
+        const uint32_t off1 = k0 + 32 < K ? base + F::kGroupB : 0u;
+        fw[slot].load2(wrow + off0, wrow + off1);
+#pragma unroll
+        for (int i = 0; i < TB; ++i) fa[slot][i].load2(arow[i] + off0, arow[i] + off1);
+    };
+    v4i acc[TB];
+#pragma unroll
+    for (int i = 0; i < TB; ++i) acc[i] = v4i{0, 0, 0, 0};
+    auto compute = [&](int kt, int slot) {
+        if (kt >= nkt) return;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            v4i wo = fw[slot].op(s);
+            if (kt * 256 + 64 * q + 32 * (s >> 1) >= K) wo = v4i{0, 0, 0, 0};
+#pragma unroll
+            for (int i = 0; i < TB; ++i)
+                acc[i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa[slot][i].op(s), wo, acc[i], 0, 0, 0);
+        }
+    };
+    load_step(w, 0);
+    load_step(w + NW, 1);
+    for (int kt = w; kt < nkt; kt += 2 * NW) {
+        compute(kt, 0);
+        load_step(kt + 2 * NW, 0);
+        compute(kt + NW, 1);
+        load_step(kt + 3 * NW, 1);
+    }
+
+    // sum the waves' partial accumulators (fixed order) and write the outputs:
+    // lane l, register v holds token 16 i + 4 (l / 16) + v, channel l % 16
+#pragma unroll
+    for (int i = 0; i < TB; ++i)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) red[w][i][v][lane] = acc[i][v];
+    __syncthreads();
+    for (int e = threadIdx.x; e < TB * 4 * 64; e += NW * 64) {
+        const int i = e / 256, v = (e / 64) % 4, ln = e % 64;
+        int a = 0;
+#pragma unroll
+        for (int ww = 0; ww < NW; ++ww) a += red[ww][i][v][ln];
+        const int tok = 16 * i + 4 * (ln >> 4) + v;
+        const int ch = bn0 + (ln & 15);
+        if (tok < n) {
+            a >>= F::kShift;
+            float val = (static_cast<float>(a) * sa[tok]) * sw[ch];
+            if (res != nullptr) val += from_out(res[static_cast<int64_t>(tok) * ld_r + ch]);
+            y[static_cast<int64_t>(tok) * ld_y + ch] = to_out<YT>(val);
+            if (acc_out != nullptr) acc_out[static_cast<int64_t>(tok) * N + ch] = a;
+        }
+    }
+}
+
+template <int BITS, int TB, int NW, typename YT>
+hipError_t launch_gemv16(const uint8_t *a, const float *sa, int64_t n, const uint8_t *w, const float *sw, int64_t N,
+                         int64_t K, void *y, int64_t ld_y, int32_t *acc_out, const void *res, int64_t ld_r,
+                         hipStream_t s) {
+    hipLaunchKernelGGL((qgemv16_kernel<BITS, TB, NW, YT>), dim3(static_cast<unsigned>(N / 16)), dim3(NW * 64), 0,
+                       s, a, sa, static_cast<int>(n), w, sw, static_cast<int>(N), static_cast<int>(K),
+                       static_cast<YT *>(y), ld_y, acc_out, static_cast<const YT *>(res), ld_r);
+    return hipGetLastError();
+}
+
 template <int BITS, int TM, typename YT>
 hipError_t launch_gemv(const uint8_t *a, const float *sa, int64_t n, const uint8_t *w, const float *sw, int64_t N,
                        int64_t K, void *y, int64_t ld_y, int32_t *acc_out, const void *res, int64_t ld_r,
@@ -509,10 +607,27 @@ template <int BITS, typename YT>
 hipError_t launch_b(const uint8_t *a, const float *sa, int64_t n, const uint8_t *w, const float *sw, int64_t N,
                     int64_t K, void *y, int64_t ld_y, int32_t *acc_out, const void *res, int64_t ld_r, hipStream_t s) {
     const int64_t cus = device_cus();
-    // decode-size batches stream the weights once: qgemv_kernel while its
-    // workgroups fit the CUs in one round (measured: faster for N = 4096 at 64
-    // tokens, slower for N = 12288 and 22016), else narrow channel tiles
+    // decode-size batches stream the weights once
     const int64_t gemv_wgs = (N + 31) / 32;
+    // up to 16 tokens, or up to 64 while 16-channel workgroups fit the CUs in
+    // one round: 16-channel workgroups on the 16 x 16 x 64 matrix core (more
+    // workgroups streaming the weights; measured faster than the kernels
+    // below for 1 and 8 tokens on every layer shape and for 64 tokens at
+    // N = 4096; slower at 64 tokens for N = 12288 and 22016, where every
+    // workgroup re-reads all 64 activation rows)
+    if (n <= 16 || (n <= 64 && N / 16 <= cus)) {
+        const bool deep = K >= 8192;
+        switch ((n + 15) / 16) {
+        case 1: return deep ? launch_gemv16<BITS, 1, 8, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s)
+                            : launch_gemv16<BITS, 1, 4, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s);
+        case 2: return deep ? launch_gemv16<BITS, 2, 8, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s)
+                            : launch_gemv16<BITS, 2, 4, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s);
+        case 3: return deep ? launch_gemv16<BITS, 3, 8, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s)
+                            : launch_gemv16<BITS, 3, 4, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s);
+        default: return deep ? launch_gemv16<BITS, 4, 8, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s)
+                             : launch_gemv16<BITS, 4, 4, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s);
+        }
+    }
     if (n <= 32) {
         if (gemv_wgs <= 2 * cus) return launch_gemv<BITS, 1, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s);
         return launch_t<BITS, 32, 32, 1, 1, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s);

@@ -190,6 +190,8 @@ GEMM_CASES = [  # bits, n, N, K, y dtype
     (4, 1, 32, 32, "f32"), (4, 5, 96, 96, "bf16"), (3, 7, 64, 224, "f32"), (4, 64, 256, 256, "bf16"),
     (3, 65, 288, 4096, "bf16"), (4, 130, 256, 4096, "f32"), (4, 33, 512, 11008, "bf16"), (3, 200, 160, 1056, "f32"),
     (4, 300, 4096, 512, "bf16"), (4, 20, 16448, 256, "bf16"), (3, 50, 8224, 224, "f32"),
+    # 16-channel decode kernel: one token block of a wide layer, int3 with a long k, three token blocks
+    (4, 16, 22016, 4096, "bf16"), (3, 12, 4096, 11008, "bf16"), (4, 40, 2048, 4128, "f32"),
 ]
 
 
