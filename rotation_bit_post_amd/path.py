@@ -13,8 +13,11 @@ zh 2.2):
           rsq_quant_act      down_proj input -> codes
           rsq_qgemm          -> y_down
 
-The attention core, SiLU * up and the residual adds are outside this path:
-the o_proj and down_proj inputs are fixed stand-ins. With ``correction=False``
+The attention core and SiLU * up are outside this path: the o_proj and
+down_proj inputs are fixed stand-ins. The residual adds are taken in with
+``stages(chain=True)``: the o_proj and down_proj outputs are added to the
+corrected residual in the GEMM epilogue (rsq_qgemm_residual) and site B reads
+the sum. With ``correction=False``
 each site runs RMSNorm + quantisation only (rsq_quant_act), the cost of a
 single global rotation (T = I), for the overhead comparison.
 
