@@ -33,7 +33,9 @@
  *    enqueues nothing); 1 <= r <= 64; bits 3 or 4. Upper limits (beyond
  *    them RSQ_ERR_UNSUPPORTED): k <= 65536 for the GEMMs (the int32
  *    accumulator bound), k <= 32768 for rsq_quant_act (one row in the
- *    registers of at most four waves), d <= 65536 for the correction.
+ *    registers of at most four waves); for the correction d / 32 must split
+ *    into at most 8 waves of 1, 2, 4, 8, 16 or 32 column chunks (at most 16
+ *    for a float32 residual), i.e. d <= 8192 (4096 for float32).
  */
 #ifndef RSQ_H
 #define RSQ_H

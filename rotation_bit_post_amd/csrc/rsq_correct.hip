@@ -30,7 +30,7 @@ namespace rsq {
 
 namespace {
 
-constexpr int kMaxWaves = 8;
+constexpr int kMaxWaves = kCorrectMaxWaves;
 
 // ------------------------------------------------------------ site layout
 // Four parts of d * r_pad bf16 each: U hi, V hi, U lo, V lo (a bf16 residual
@@ -557,20 +557,6 @@ int device_cus() {
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
     if (dev < 64) cached[dev] = cus;
     return cus;
-}
-
-bool correct_geometry(int64_t d, bool f32, int *waves, int *chunks_per_wave) {
-    if (d <= 0 || d % 32) return false;
-    const int64_t nch = d / 32;
-    for (int cpw : {1, 2, 4, 8, 16, 32}) {
-        if (f32 && cpw > 16) break;  // a float32 slice of 32 chunks does not fit in registers
-        if (nch % cpw == 0 && nch / cpw <= kMaxWaves) {
-            *waves = static_cast<int>(nch / cpw);
-            *chunks_per_wave = cpw;
-            return true;
-        }
-    }
-    return false;
 }
 
 hipError_t launch_site_prepare(const float *U, const float *M, int d, int r, void *site, hipStream_t s) {

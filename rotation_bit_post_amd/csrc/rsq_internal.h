@@ -13,10 +13,26 @@ inline int rank_pad(int r) { return (r + 31) / 32 * 32; }
 // (parts U hi, V hi, U lo, V lo).
 inline size_t site_bytes(int64_t d, int r) { return static_cast<size_t>(d) * rank_pad(r) * 2 * 2 * 2; }
 
+// Most waves in a correction workgroup.
+constexpr int kCorrectMaxWaves = 8;
+
 // Waves per workgroup and 32-column chunks per wave of the correction kernel
-// for width d (f32: float32 residual, at most 16 chunks per wave); returns
-// false if d cannot be split evenly.
-bool correct_geometry(int64_t d, bool f32, int *waves, int *chunks_per_wave);
+// for width d: the fewest chunks per wave (1, 2, 4, ... 32; at most 16 for a
+// float32 residual, whose slice of 32 chunks does not fit in registers) that
+// split d / 32 evenly over at most kCorrectMaxWaves waves. False if none does.
+inline bool correct_geometry(int64_t d, bool f32, int *waves, int *chunks_per_wave) {
+    if (d <= 0 || d % 32) return false;
+    const int64_t nch = d / 32;
+    for (int cpw : {1, 2, 4, 8, 16, 32}) {
+        if (f32 && cpw > 16) break;
+        if (nch % cpw == 0 && nch / cpw <= kCorrectMaxWaves) {
+            *waves = static_cast<int>(nch / cpw);
+            *chunks_per_wave = cpw;
+            return true;
+        }
+    }
+    return false;
+}
 
 // Compute units of the current device (cached per device).
 int device_cus();
