@@ -23,6 +23,8 @@
 // chosen for V, also the accumulator layout of the reprojection.
 #include <type_traits>
 
+#include <atomic>
+
 #include "rsq_device.h"
 #include "rsq_internal.h"
 
@@ -549,13 +551,18 @@ hipError_t launch_c(int cpw, int r32, const void *h_in, void *h_out, int64_t n, 
 }  // namespace
 
 int device_cus() {
-    static int cached[64] = {0};
+    // per-device cache; callers on several threads may fill it concurrently
+    // (they store the same value)
+    static std::atomic<int> cached[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
-    if (dev < 64 && cached[dev] > 0) return cached[dev];
+    if (dev < 64) {
+        const int c = cached[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
     int cus = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-    if (dev < 64) cached[dev] = cus;
+    if (dev < 64) cached[dev].store(cus, std::memory_order_relaxed);
     return cus;
 }
 
