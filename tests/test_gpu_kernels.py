@@ -68,6 +68,7 @@ CORRECT_CASES = [  # dtype, d, r, n
     ("f32", 256, 8, 16), ("f32", 256, 8, 3), ("bf16", 256, 8, 17), ("bf16", 96, 8, 7),
     ("bf16", 1024, 32, 33), ("bf16", 512, 64, 40), ("f32", 128, 16, 5), ("bf16", 2048, 2, 1),
     ("f32", 1024, 40, 19),
+    ("f32", 4096, 32, 20),   # the widest float32 residual
 ]
 
 
@@ -76,7 +77,7 @@ def test_subspace_correct_matches_oracle(dtype, d, r, n):
     rsq = lib()
     import torch
     print(f"case correct dtype={dtype} d={d} r={r} n={n}", flush=True)
-    U, M = random_site(d, r, seed=d + r)
+    U, M = random_site(d, r, seed=d + r) if d <= 2048 else subspace_site(d, r, seed=d + r)
     h = residual(n, d, dtype, seed=n)
     site = gpu_site(U, M)
     hd = to_dev(h, dtype)
@@ -141,6 +142,8 @@ QUANT_CASES = [  # dtype, n, k, bits, norm, weighted
     ("bf16", 7, 4096, 4, True, False), ("bf16", 64, 4096, 3, True, False), ("f32", 16, 256, 4, True, False),
     ("bf16", 5, 11008, 4, False, False), ("bf16", 3, 14336, 3, False, False), ("f32", 9, 96, 3, True, True),
     ("bf16", 33, 1024, 4, True, True), ("bf16", 2, 28672, 4, False, False), ("f32", 130, 32, 4, False, False),
+    # the longest rows the kernel takes (four waves of 16 chunks per lane)
+    ("bf16", 3, 32768, 4, True, True), ("f32", 4, 32768, 3, True, False),
 ]
 
 
@@ -240,6 +243,37 @@ def test_qgemm_bit_exact(bits, n, N, K, ydt):
     rsq.rsq_qgemm(a_dev, to_dev(sa, "f32"), n, w_dev, to_dev(sw, "f32"), N, K, bits, y2)
     torch.cuda.synchronize()
     assert torch.equal(y, y2)
+
+
+@pytest.mark.parametrize("bits,n,N,K,ydt", [(4, 40, 64, 65536, "f32"), (3, 300, 256, 65536, "bf16"),
+                                             (4, 300, 96, 65536, "bf16")])
+def test_qgemm_longest_k_with_extreme_accumulators(bits, n, N, K, ydt):
+    """K at its limit, with rows of -qmax against rows of -qmax and +qmax.
+
+    Accumulator 0,0 is K qmax^2 and 0,1 is -K qmax^2, the largest magnitudes
+    the codes allow (the widened products then sum to 256 or 1024 times that,
+    still inside int32); the decode kernel takes 40 tokens, the tiles 300.
+    """
+    rsq = lib()
+    import torch
+    print(f"case qgemm longest k bits={bits} n={n} N={N} K={K} y={ydt}", flush=True)
+    rng = np.random.default_rng(K + n)
+    qm = packing.qmax(bits)
+    qa, qw = _random_codes(n, K, bits, rng, extremes=False), _random_codes(N, K, bits, rng, extremes=False)
+    qa[0] = -qm
+    qw[0] = -qm
+    qw[1] = qm
+    sa = rng.uniform(0.01, 2.0, n).astype(np.float32)
+    sw = rng.uniform(1e-3, 1e-2, N).astype(np.float32)
+    y = torch.empty((n, N), dtype=torch.bfloat16 if ydt == "bf16" else torch.float32, device="cuda")
+    acc = torch.empty((n, N), dtype=torch.int32, device="cuda")
+    rsq.rsq_qgemm(torch.from_numpy(packing.pack(qa, bits)).cuda(), to_dev(sa, "f32"), n,
+                  torch.from_numpy(packing.pack(qw, bits)).cuda(), to_dev(sw, "f32"), N, K, bits, y, acc_out=acc)
+    torch.cuda.synchronize()
+    acc_ref = online.gemm(qa, qw)
+    assert acc_ref[0, 0] == K * qm * qm and acc_ref[0, 1] == -K * qm * qm
+    assert np.array_equal(acc.cpu().numpy().astype(np.int64), acc_ref)
+    assert np.array_equal(to_host(y).astype(np.float64), np.asarray(online.dequant(acc_ref, sa, sw, ydt), np.float64))
 
 
 @pytest.mark.parametrize("bits,n,N,K", [(4, 1000, 12320, 4096), (4, 2000, 22048, 1056), (3, 2000, 22048, 4096),
