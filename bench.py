@@ -32,6 +32,7 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix-core peak
 INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 matrix-core peak
+FP4_PEAK_TOPS = 10100.0        # MI355X dense fp4 (and fp6) matrix-core peak
 METRIC = "tokens/s per decoder-layer linear path (W4A4, D=4096, r=32); % HBM / MFMA peak"
 
 
@@ -341,6 +342,7 @@ def main():
 
     stages_out = {}
     gemm_ops = gemm_ms = gemm_launches = 0
+    gemm_peak = FP4_PEAK_TOPS if base.fp4 else INT8_PEAK_TOPS
     for nm in names:
         byts, ops = base.stage_work(nm)
         t = sum(stage_ms[nm]) / args.steps
@@ -348,7 +350,7 @@ def main():
         rec["hbm_frac"] = round(byts / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
         if ops:
             rec["alg_ops"] = ops
-            rec["mfma_frac"] = round(ops / (t * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4)
+            rec["mfma_frac"] = round(ops / (t * 1e-3) / 1e12 / gemm_peak, 4)
             gemm_ops += ops
             gemm_ms += t
             gemm_launches += 1
@@ -370,7 +372,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int8",
+        "dtype": "fp4" if base.fp4 else "int8",
         "data": "synthetic (seeded N(0,1) residual with outlier channels, Hadamard*Cayley rotations, N(0,sigma) weights; no dataset, no trained weights)",
         "config": {
             "workload": f"{cfg.name}: D={cfg.D}, FFN={cfg.F}, r={base.r}, {n} tokens, {cfg.h_dtype} residual, "
@@ -380,12 +382,13 @@ def main():
             "tokens": n, "D": cfg.D, "ffn": cfg.F, "r": base.r, "bits": cfg.bits, "buffer_copies": len(copies),
         },
         "roofline": {
-            "kernel": "qgemm_kernel (int4 codes on v_mfma_i32_32x32x32_i8), all 4 launches of a step",
+            "kernel": ("qgemm_kernel (3-bit codes as fp4 on v_mfma_scale_f32_32x32x64_f8f6f4)" if base.fp4 else
+                       f"qgemm_kernel (int{cfg.bits} codes on v_mfma_i32_32x32x32_i8)") + ", all 4 launches of a step",
             "bound": "mfma",
             "achieved": round(achieved, 2),
-            "peak": INT8_PEAK_TOPS,
+            "peak": gemm_peak,
             "unit": "TOP/s",
-            "frac": round(achieved / INT8_PEAK_TOPS, 4),
+            "frac": round(achieved / gemm_peak, 4),
             "traffic": traffic,
             "avg_launch_ms": round(gemm_ms / max(gemm_launches, 1), 5),
         },
@@ -399,7 +402,7 @@ def main():
         "layer_chained": None if ms_chain is None else {
             "ms_per_step": round(ms_chain, 5),
             "tokens_per_s": round(n / (ms_chain * 1e-3), 1),
-            "note": "the same eight stages with the residual stream carried through: o_proj and down_proj "
+            "note": "the same stages with the residual stream carried through: o_proj and down_proj "
                     "outputs added to the corrected residual inside the GEMM epilogue (rsq_qgemm_residual), "
                     "site B reading h2; timed back to back, no events between stages",
         },
@@ -409,7 +412,7 @@ def main():
             "graph_outputs_identical": graph_ok,
             "value_from": "graph" if ms_per_step != ms_eager else "eager",
             "step_ms_p10_p50_p90": [pct(0.1), pct(0.5), pct(0.9)],
-            "note": "eager: the eight launches back to back; graph: the same launches recorded once as a HIP "
+            "note": "eager: the step's launches back to back; graph: the same launches recorded once as a HIP "
                     "graph and replayed (outputs checked bit-identical first); value uses the faster; "
                     "percentiles: single steps of the per-stage pass (events between stages add a little)",
         },

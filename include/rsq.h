@@ -29,6 +29,11 @@
  *              slots 1,3,5: bits 2-4 of lane b of word (j-1)/2;
  *              slot 6: u bits 0-1 -> bits 0-1 of lane b of w0, u bit 2 -> bit 1 of lane b of w2;
  *              slot 7: u bits 0-1 -> bits 0-1 of lane b of w1, u bit 2 -> bit 0 of lane b of w2.
+ *  - fp4 codes (rsq_codes_to_fp4, rsq_qgemm_fp4): 3-bit codes c in [-3, 3]
+ *    held as OCP MX fp4 (e2m1) values c / 2, one nibble each (bit 3 the sign,
+ *    bits 0-1 |c|, bit 2 zero), k / 2 bytes per row; each group of 32 codes
+ *    (the int3 group above) takes 16 bytes: byte 4i + b (i, b < 4) holds
+ *    code 8i + b in bits 4-7 and code 8i + 4 + b in bits 0-3.
  *  - Sizes: d and k multiples of 32; n_out a multiple of 32; n >= 0 (n = 0
  *    enqueues nothing); 1 <= r <= 64; bits 3 or 4. Upper limits (beyond
  *    them RSQ_ERR_UNSUPPORTED): k <= 65536 for the GEMMs (the int32
@@ -160,6 +165,33 @@ rsq_status rsq_qgemm_residual(const uint8_t *a_codes, const float *a_scales, int
                               const uint8_t *w_codes, const float *w_scales, int64_t n_out,
                               int64_t k, int bits, const void *residual, int64_t ld_r,
                               void *y, int y_dtype, int64_t ld_y, void *stream);
+
+/*
+ * 3-bit codes in another layout for the fp4 matrix cores: each of `rows`
+ * packed int3 rows of k codes (rsq_packed_row_bytes(k, 3) bytes, contiguous)
+ * becomes a row of k / 2 bytes of fp4 codes (contiguous), the same values.
+ * Weights are converted once; activation codes once per linear (a pass over
+ * the codes, far cheaper than converting inside the GEMM, where every
+ * workgroup of a row of tiles would convert the same codes again).
+ * codes, fp4: 16-byte aligned, not overlapping.
+ */
+rsq_status rsq_codes_to_fp4(const uint8_t *codes, int64_t rows, int64_t k, uint8_t *fp4, void *stream);
+
+/*
+ * The W3A3 quantised linear (zh 4 and fr 4; the linear of zh 2.2 and nl 2A)
+ * on fp4 codes: rsq_qgemm (bits 3) and, with residual non-NULL,
+ * rsq_qgemm_residual, on the same codes in the fp4 layout; y and acc_out
+ * are identical to theirs. The matrix cores multiply c_a / 2 by c_w / 2 with
+ * a block scale of 2 on each side, so every product is c_a c_w exactly and
+ * every partial sum an integer below 2^24, exact in their float32
+ * accumulation.
+ * a_fp4: n rows of k / 2 bytes; w_fp4: n_out rows of k / 2 bytes.
+ * residual: NULL, or as in rsq_qgemm_residual (stride ld_r; may be y).
+ * acc_out: NULL, or n x n_out int32 (contiguous).
+ */
+rsq_status rsq_qgemm_fp4(const uint8_t *a_fp4, const float *a_scales, int64_t n, const uint8_t *w_fp4,
+                         const float *w_scales, int64_t n_out, int64_t k, const void *residual, int64_t ld_r, void *y,
+                         int y_dtype, int64_t ld_y, int32_t *acc_out, void *stream);
 
 /*
  * One correction site feeding its quantised linear: rsq_correct_quant then

@@ -14,6 +14,12 @@ int3: a row of K codes (K a multiple of 32) becomes 3K/8 bytes, 12 per group
         j = 1, 3, 5 : bits 2-4 of lane b of word (j-1)/2
         j = 6       : u bits 0-1 in bits 0-1 of lane b of w0, u bit 2 in bit 1 of lane b of w2
         j = 7       : u bits 0-1 in bits 0-1 of lane b of w1, u bit 2 in bit 0 of lane b of w2
+fp4:  3-bit codes c in [-3, 3] as fp4 E2M1 values c/2 (the element format of
+      the OCP Microscaling (MX) specification v1.0: 1 sign bit, 2 exponent
+      bits with bias 1, 1 mantissa bit; exponent 0 is subnormal). A row of K
+      codes (K a multiple of 32) becomes K/2 bytes, 16 per group of 32 codes:
+      byte 4i + b (i, b < 4) holds code 8i + b in bits 4-7 and code 8i + 4 + b
+      in bits 0-3 (the same codes as the int3 group's slots 2i and 2i+1).
 """
 from __future__ import annotations
 
@@ -95,3 +101,57 @@ def unpack(packed, k: int, bits: int) -> np.ndarray:
             lo_word, hi_bit = (0, 1) if j == 6 else (1, 0)
             u[:, i::32] = (p[:, cols(lo_word)] & 3) | (((p[:, cols(2)] >> hi_bit) & 1) << 2)
     return _signed(u, 3)
+
+
+def e2m1_value(nibble: int) -> float:
+    """Value of a 4-bit E2M1 element (OCP MX v1.0): sign, 2-bit exponent (bias 1), 1-bit mantissa."""
+    if not 0 <= nibble < 16:
+        raise ValueError("not a 4-bit pattern")
+    sign = -1.0 if nibble & 8 else 1.0
+    e, m = (nibble >> 1) & 3, nibble & 1
+    if e == 0:
+        return sign * (m / 2.0)              # subnormal: 2^(1-bias) * 0.m
+    return sign * 2.0 ** (e - 1) * (1.0 + m / 2.0)
+
+
+def _fp4_nibble(code: int) -> int:
+    """The E2M1 pattern whose value is code/2 (zero as +0); found by decoding every pattern."""
+    target = code / 2.0
+    for nib in range(16):
+        if e2m1_value(nib) == target and not (target == 0 and nib != 0):
+            return nib
+    raise ValueError(f"code {code} is not exact in E2M1 as code/2")
+
+
+def pack_fp4(codes) -> np.ndarray:
+    """Pack a (rows, K) array of 3-bit codes into (rows, K/2) uint8 fp4 rows (layout above)."""
+    c = np.atleast_2d(np.asarray(codes, dtype=np.int64))
+    rows, k = c.shape
+    if k % 32:
+        raise ValueError("fp4 rows need a multiple of 32 codes")
+    if np.any(np.abs(c) > 3):
+        raise ValueError("code out of range")
+    nib = np.vectorize(_fp4_nibble, otypes=[np.int64])(c) if c.size else c
+    out = np.zeros((rows, k // 2), dtype=np.int64)
+    for i in range(4):
+        for b in range(4):
+            hi, lo = nib[:, 8 * i + b::32], nib[:, 8 * i + 4 + b::32]   # (rows, K/32)
+            out[:, 16 * np.arange(k // 32) + 4 * i + b] = (hi << 4) | lo
+    return out.astype(np.uint8)
+
+
+def unpack_fp4(packed, k: int) -> np.ndarray:
+    """Inverse of ``pack_fp4``: (rows, K/2) uint8 -> (rows, K) int64 codes (2 x the E2M1 value)."""
+    p = np.atleast_2d(np.asarray(packed, dtype=np.int64))
+    if k % 32 or p.shape[1] != k // 2:
+        raise ValueError("packed width does not match K")
+    value2 = np.array([2.0 * e2m1_value(n) for n in range(16)])
+    c = np.zeros((p.shape[0], k), dtype=np.float64)
+    for i in range(4):
+        for b in range(4):
+            byte = p[:, 16 * np.arange(k // 32) + 4 * i + b]
+            c[:, 8 * i + b::32] = value2[(byte >> 4) & 0xF]
+            c[:, 8 * i + 4 + b::32] = value2[byte & 0xF]
+    if np.any(c != np.rint(c)) or np.any(np.abs(c) > 3):
+        raise ValueError("not a 3-bit code")
+    return c.astype(np.int64)

@@ -49,6 +49,8 @@ def _load() -> C.CDLL:
         "rsq_qgemm": (i32, [vp, vp, i64, vp, vp, i64, i64, i32, vp, i32, i64, vp, vp]),
         "rsq_qgemm_residual": (i32, [vp, vp, i64, vp, vp, i64, i64, i32, vp, i64, vp, i32, i64, vp]),
         "rsq_layer_fused": (i32, [vp, vp, i32, i64, i64, vp, i32, vp, f32, i32, vp, vp, vp, vp, i64, vp, i32, vp]),
+        "rsq_codes_to_fp4": (i32, [vp, i64, i64, vp, vp]),
+        "rsq_qgemm_fp4": (i32, [vp, vp, i64, vp, vp, i64, i64, vp, i64, vp, i32, i64, vp, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -59,7 +61,7 @@ def _load() -> C.CDLL:
 LIB = _load()
 EXPORTS = ("rsq_version", "rsq_status_str", "rsq_last_error", "rsq_packed_row_bytes", "rsq_site_bytes",
            "rsq_site_prepare", "rsq_subspace_correct", "rsq_quant_act", "rsq_correct_quant", "rsq_qgemm", "rsq_qgemm_residual",
-           "rsq_layer_fused")
+           "rsq_layer_fused", "rsq_codes_to_fp4", "rsq_qgemm_fp4")
 
 
 def _check(status: int, func: str) -> None:
@@ -149,6 +151,21 @@ def rsq_qgemm_residual(a_codes, a_scales, n: int, w_codes, w_scales, n_out: int,
     _check(LIB.rsq_qgemm_residual(_ptr(a_codes), _ptr(a_scales), n, _ptr(w_codes), _ptr(w_scales), n_out, k, bits,
                                   _ptr(residual), residual.stride(0), _ptr(y), _dtype_code(y), y.stride(0),
                                   _stream(stream)), "rsq_qgemm_residual")
+
+
+def rsq_codes_to_fp4(codes, rows: int, k: int, fp4, stream=None) -> None:
+    """Packed int3 rows -> fp4 rows (k / 2 bytes each), the same code values."""
+    _check(LIB.rsq_codes_to_fp4(_ptr(codes), rows, k, _ptr(fp4), _stream(stream)), "rsq_codes_to_fp4")
+
+
+def rsq_qgemm_fp4(a_fp4, a_scales, n: int, w_fp4, w_scales, n_out: int, k: int, y, residual=None, acc_out=None,
+                  stream=None) -> None:
+    """The 3-bit quantised linear on fp4 codes; residual (optional) may be y itself."""
+    if residual is not None and residual.dtype != y.dtype:
+        raise ValueError("residual and y must have the same dtype")
+    _check(LIB.rsq_qgemm_fp4(_ptr(a_fp4), _ptr(a_scales), n, _ptr(w_fp4), _ptr(w_scales), n_out, k, _ptr(residual),
+                             residual.stride(0) if residual is not None else 0, _ptr(y), _dtype_code(y), y.stride(0),
+                             _ptr(acc_out), _stream(stream)), "rsq_qgemm_fp4")
 
 
 def rsq_layer_fused(h_in, h_out, site, r: int, codes, scales, w_codes, w_scales, n_out: int, y, bits: int,

@@ -86,6 +86,43 @@ rsq_status check_quant_out(int64_t n, int64_t k, int bits, const uint8_t *codes,
     return RSQ_OK;
 }
 
+// Sizes, pointers and alignment shared by the quantised linears.
+rsq_status check_gemm(int64_t n, int64_t n_out, int64_t k, int y_dtype, int64_t ld_y, const void *a_codes,
+                      const float *a_scales, const void *w_codes, const float *w_scales, const void *y) {
+    RSQ_CHECK(dtype_ok(y_dtype), RSQ_ERR_INVALID_ARG, "y_dtype = %d is not RSQ_F32 or RSQ_BF16", y_dtype);
+    RSQ_CHECK(n >= 0, RSQ_ERR_INVALID_ARG, "n = %lld is negative", (long long)n);
+    RSQ_CHECK(n_out > 0 && n_out % 32 == 0, RSQ_ERR_INVALID_ARG, "n_out = %lld must be a positive multiple of 32", (long long)n_out);
+    RSQ_CHECK(k > 0 && k % 32 == 0, RSQ_ERR_INVALID_ARG, "k = %lld must be a positive multiple of 32", (long long)k);
+    RSQ_CHECK(k <= 65536, RSQ_ERR_UNSUPPORTED, "k = %lld exceeds 65536 (int32 accumulator bound)", (long long)k);
+    RSQ_CHECK(ld_y >= n_out, RSQ_ERR_INVALID_ARG, "ld_y = %lld < n_out = %lld", (long long)ld_y, (long long)n_out);
+    RSQ_CHECK(n <= 0x7fffffff && n_out <= 0x7fffffff, RSQ_ERR_UNSUPPORTED, "size too large");
+    if (n == 0) return RSQ_OK;
+    RSQ_CHECK(a_codes && a_scales && w_codes && w_scales && y, RSQ_ERR_INVALID_ARG, "null pointer");
+    RSQ_CHECK(aligned16(a_codes) && aligned16(w_codes) && aligned16(a_scales) && aligned16(w_scales) && aligned16(y),
+              RSQ_ERR_INVALID_ARG, "operands must be 16-byte aligned");
+    return RSQ_OK;
+}
+
+// The residual of a linear: n rows of n_out values of y_dtype, stride ld_r;
+// either y itself (same stride) or disjoint from it.
+rsq_status check_residual(int64_t n, int64_t n_out, int y_dtype, const void *residual, int64_t ld_r, const void *y,
+                          int64_t ld_y) {
+    RSQ_CHECK(ld_r >= n_out, RSQ_ERR_INVALID_ARG, "ld_r = %lld < n_out = %lld", (long long)ld_r, (long long)n_out);
+    if (n == 0) return RSQ_OK;
+    RSQ_CHECK(residual != nullptr && aligned16(residual), RSQ_ERR_INVALID_ARG, "residual must be non-null and 16-byte aligned");
+    if (residual != y) {
+        const size_t es = dtype_size(y_dtype);
+        const char *a = static_cast<const char *>(residual), *b = static_cast<const char *>(y);
+        const size_t span_r = static_cast<size_t>((n - 1) * ld_r + n_out) * es;
+        const size_t span_y = static_cast<size_t>((n - 1) * ld_y + n_out) * es;
+        RSQ_CHECK(a + span_r <= b || b + span_y <= a, RSQ_ERR_INVALID_ARG,
+                  "residual and y overlap without being the same buffer");
+    } else {
+        RSQ_CHECK(ld_r == ld_y, RSQ_ERR_INVALID_ARG, "in place (residual == y) needs ld_r == ld_y");
+    }
+    return RSQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -177,17 +214,8 @@ rsq_status rsq_qgemm(const uint8_t *a_codes, const float *a_scales, int64_t n, c
     g_last_error[0] = 0;
     rsq_status st = check_bits(bits);
     if (st != RSQ_OK) return st;
-    RSQ_CHECK(dtype_ok(y_dtype), RSQ_ERR_INVALID_ARG, "y_dtype = %d is not RSQ_F32 or RSQ_BF16", y_dtype);
-    RSQ_CHECK(n >= 0, RSQ_ERR_INVALID_ARG, "n = %lld is negative", (long long)n);
-    RSQ_CHECK(n_out > 0 && n_out % 32 == 0, RSQ_ERR_INVALID_ARG, "n_out = %lld must be a positive multiple of 32", (long long)n_out);
-    RSQ_CHECK(k > 0 && k % 32 == 0, RSQ_ERR_INVALID_ARG, "k = %lld must be a positive multiple of 32", (long long)k);
-    RSQ_CHECK(k <= 65536, RSQ_ERR_UNSUPPORTED, "k = %lld exceeds 65536 (int32 accumulator bound)", (long long)k);
-    RSQ_CHECK(ld_y >= n_out, RSQ_ERR_INVALID_ARG, "ld_y = %lld < n_out = %lld", (long long)ld_y, (long long)n_out);
-    RSQ_CHECK(n <= 0x7fffffff && n_out <= 0x7fffffff, RSQ_ERR_UNSUPPORTED, "size too large");
-    if (n == 0) return RSQ_OK;
-    RSQ_CHECK(a_codes && a_scales && w_codes && w_scales && y, RSQ_ERR_INVALID_ARG, "null pointer");
-    RSQ_CHECK(aligned16(a_codes) && aligned16(w_codes) && aligned16(a_scales) && aligned16(w_scales) && aligned16(y),
-              RSQ_ERR_INVALID_ARG, "operands must be 16-byte aligned");
+    st = check_gemm(n, n_out, k, y_dtype, ld_y, a_codes, a_scales, w_codes, w_scales, y);
+    if (st != RSQ_OK || n == 0) return st;
     RSQ_CHECK(acc_out == nullptr || aligned16(acc_out), RSQ_ERR_INVALID_ARG, "acc_out must be 16-byte aligned");
     return hip_status(rsq::launch_qgemm(a_codes, a_scales, n, w_codes, w_scales, n_out, k, bits, y, y_dtype, ld_y,
                                         acc_out, nullptr, 0, static_cast<hipStream_t>(stream)),
@@ -200,32 +228,47 @@ rsq_status rsq_qgemm_residual(const uint8_t *a_codes, const float *a_scales, int
     g_last_error[0] = 0;
     rsq_status st = check_bits(bits);
     if (st != RSQ_OK) return st;
-    RSQ_CHECK(dtype_ok(y_dtype), RSQ_ERR_INVALID_ARG, "y_dtype = %d is not RSQ_F32 or RSQ_BF16", y_dtype);
-    RSQ_CHECK(n >= 0, RSQ_ERR_INVALID_ARG, "n = %lld is negative", (long long)n);
-    RSQ_CHECK(n_out > 0 && n_out % 32 == 0, RSQ_ERR_INVALID_ARG, "n_out = %lld must be a positive multiple of 32", (long long)n_out);
-    RSQ_CHECK(k > 0 && k % 32 == 0, RSQ_ERR_INVALID_ARG, "k = %lld must be a positive multiple of 32", (long long)k);
-    RSQ_CHECK(k <= 65536, RSQ_ERR_UNSUPPORTED, "k = %lld exceeds 65536 (int32 accumulator bound)", (long long)k);
-    RSQ_CHECK(ld_y >= n_out, RSQ_ERR_INVALID_ARG, "ld_y = %lld < n_out = %lld", (long long)ld_y, (long long)n_out);
-    RSQ_CHECK(ld_r >= n_out, RSQ_ERR_INVALID_ARG, "ld_r = %lld < n_out = %lld", (long long)ld_r, (long long)n_out);
-    RSQ_CHECK(n <= 0x7fffffff && n_out <= 0x7fffffff, RSQ_ERR_UNSUPPORTED, "size too large");
-    if (n == 0) return RSQ_OK;
-    RSQ_CHECK(a_codes && a_scales && w_codes && w_scales && y && residual, RSQ_ERR_INVALID_ARG, "null pointer");
-    RSQ_CHECK(aligned16(a_codes) && aligned16(w_codes) && aligned16(a_scales) && aligned16(w_scales) && aligned16(y) &&
-                  aligned16(residual),
-              RSQ_ERR_INVALID_ARG, "operands must be 16-byte aligned");
-    if (residual != y) {
-        const size_t es = dtype_size(y_dtype);
-        const char *a = static_cast<const char *>(residual), *b = static_cast<const char *>(y);
-        const size_t span_r = static_cast<size_t>((n - 1) * ld_r + n_out) * es;
-        const size_t span_y = static_cast<size_t>((n - 1) * ld_y + n_out) * es;
-        RSQ_CHECK(a + span_r <= b || b + span_y <= a, RSQ_ERR_INVALID_ARG,
-                  "residual and y overlap without being the same buffer");
-    } else {
-        RSQ_CHECK(ld_r == ld_y, RSQ_ERR_INVALID_ARG, "in place (residual == y) needs ld_r == ld_y");
-    }
+    st = check_gemm(n, n_out, k, y_dtype, ld_y, a_codes, a_scales, w_codes, w_scales, y);
+    if (st != RSQ_OK) return st;
+    st = check_residual(n, n_out, y_dtype, residual, ld_r, y, ld_y);
+    if (st != RSQ_OK || n == 0) return st;
     return hip_status(rsq::launch_qgemm(a_codes, a_scales, n, w_codes, w_scales, n_out, k, bits, y, y_dtype, ld_y,
                                         nullptr, residual, ld_r, static_cast<hipStream_t>(stream)),
                       "rsq_qgemm_residual launch");
+}
+
+rsq_status rsq_codes_to_fp4(const uint8_t *codes, int64_t rows, int64_t k, uint8_t *fp4, void *stream) {
+    g_last_error[0] = 0;
+    RSQ_CHECK(rows >= 0, RSQ_ERR_INVALID_ARG, "rows = %lld is negative", (long long)rows);
+    RSQ_CHECK(k > 0 && k % 32 == 0, RSQ_ERR_INVALID_ARG, "k = %lld must be a positive multiple of 32", (long long)k);
+    RSQ_CHECK(rows <= ((int64_t)1 << 40) / k, RSQ_ERR_UNSUPPORTED, "rows x k too large");
+    if (rows == 0) return RSQ_OK;
+    RSQ_CHECK(codes && fp4, RSQ_ERR_INVALID_ARG, "null pointer (codes or fp4)");
+    RSQ_CHECK(aligned16(codes) && aligned16(fp4), RSQ_ERR_INVALID_ARG, "codes and fp4 must be 16-byte aligned");
+    const char *a = reinterpret_cast<const char *>(codes), *b = reinterpret_cast<const char *>(fp4);
+    const size_t span_in = static_cast<size_t>(rows) * (static_cast<size_t>(k) * 3 / 8);
+    const size_t span_out = static_cast<size_t>(rows) * (static_cast<size_t>(k) / 2);
+    RSQ_CHECK(a + span_in <= b || b + span_out <= a, RSQ_ERR_INVALID_ARG, "codes and fp4 overlap");
+    return hip_status(rsq::launch_codes_to_fp4(codes, rows, k, fp4, static_cast<hipStream_t>(stream)),
+                      "rsq_codes_to_fp4 launch");
+}
+
+rsq_status rsq_qgemm_fp4(const uint8_t *a_fp4, const float *a_scales, int64_t n, const uint8_t *w_fp4,
+                         const float *w_scales, int64_t n_out, int64_t k, const void *residual, int64_t ld_r, void *y,
+                         int y_dtype, int64_t ld_y, int32_t *acc_out, void *stream) {
+    g_last_error[0] = 0;
+    rsq_status st = check_gemm(n, n_out, k, y_dtype, ld_y, a_fp4, a_scales, w_fp4, w_scales, y);
+    if (st != RSQ_OK) return st;
+    if (residual != nullptr) {
+        st = check_residual(n, n_out, y_dtype, residual, ld_r, y, ld_y);
+        if (st != RSQ_OK) return st;
+    }
+    if (n == 0) return RSQ_OK;
+    RSQ_CHECK(acc_out == nullptr || aligned16(acc_out), RSQ_ERR_INVALID_ARG, "acc_out must be 16-byte aligned");
+    return hip_status(rsq::launch_qgemm(a_fp4, a_scales, n, w_fp4, w_scales, n_out, k, rsq::kFp4, y, y_dtype, ld_y,
+                                        acc_out, residual, residual != nullptr ? ld_r : 0,
+                                        static_cast<hipStream_t>(stream)),
+                      "rsq_qgemm_fp4 launch");
 }
 
 rsq_status rsq_layer_fused(const void *h_in, void *h_out, int h_dtype, int64_t n, int64_t d, const void *site, int r,

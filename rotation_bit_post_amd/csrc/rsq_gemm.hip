@@ -18,6 +18,21 @@
 // Matrix-core roles: A = activations (rows = tokens), B = weights (columns =
 // output channels). The epilogue stages the bf16 tile in LDS and writes it
 // with 16-byte row-contiguous stores.
+//
+// 3-bit codes held as fp4 (rsq_qgemm_fp4) take the MX matrix cores: a code c
+// in [-3, 3] is exact in fp4 e2m1 as c / 2 (sign and magnitude, 0.5 steps), so
+// with a block scale of 2 on both operands v_mfma_scale_f32_32x32x64_f8f6f4
+// multiplies the codes themselves. Every product is an integer of magnitude
+// at most 9 and every partial sum at most 9 K <= 589824 < 2^24, so the
+// float32 accumulation is exact in any order and converts back to the same
+// int32 sums. The fp4 multiply takes 64 codes per instruction at the rate the
+// int8 one takes 32; the fp4 tiles go into LDS as loaded (half the LDS bytes
+// per code of the widened int8 tiles, no widening). Turning int3 codes into
+// fp4 costs more per code than widening them, so it is a pass of its own
+// (codes_to_fp4_kernel), once per activation matrix and once per weight.
+#include <algorithm>
+#include <type_traits>
+
 #include "rsq_device.h"
 #include "rsq_internal.h"
 
@@ -37,6 +52,10 @@ template <> struct Fmt<4> {
 template <> struct Fmt<3> {
     static constexpr int kGroupB = 12;
     static constexpr int kShift = 10;    // (32 a)(32 w) = 1024 a w
+};
+template <> struct Fmt<kFp4> {
+    static constexpr int kGroupB = 16;   // 32 nibbles
+    static constexpr int kShift = 0;     // the matrix core multiplies the codes themselves
 };
 
 template <typename YT> __device__ __forceinline__ YT to_out(float v);
@@ -76,6 +95,13 @@ template <> struct Group<3> {
         hi = unpack_int3_half(w0, w1, w2, 1);
     }
 };
+template <> struct Group<kFp4> {
+    v4u x;
+    __device__ __forceinline__ void load(const uint8_t *p) { x = *reinterpret_cast<const v4u *>(p); }
+    __device__ __forceinline__ void keep_if(bool ok) {
+        x = v4u{ok ? x[0] : 0u, ok ? x[1] : 0u, ok ? x[2] : 0u, ok ? x[3] : 0u};
+    }
+};
 
 // Tile order. The hardware deals workgroups round-robin to the 8 XCDs
 // (block b runs on XCD b % 8), each with its own L2. Block b is given a tile
@@ -92,12 +118,18 @@ __device__ __forceinline__ int xcd_tile(int bid, int tiles) {
 // BM tokens x BN channels per workgroup, WM x WN waves, each wave
 // (BM / WM) x (BN / WN) as TM x TN fragments of 32 x 32. Codes are widened to
 // int8 once, on their way into LDS; the inner loop is 16-byte LDS reads
-// straight into v_mfma_i32_32x32x32_i8.
+// straight into v_mfma_i32_32x32x32_i8. fp4 codes (BITS = kFp4) go into LDS
+// as loaded, a k step is 256 codes (the same 128 LDS bytes per row) and each
+// 16-byte read feeds v_mfma_scale_f32_32x32x64_f8f6f4.
 template <int BITS, int BM, int BN, int WM, int WN, int P>
 struct GemmTile {
     using F = Fmt<BITS>;
+    static constexpr bool MX = BITS == kFp4;
+    using Acc = typename std::conditional<MX, v16f, v16i>::type;
+    static constexpr int KB = MX ? 2 * kBK : kBK;         // codes per k step
+    static constexpr int GB = MX ? 16 : 32;               // LDS bytes of one 32-code group
     static constexpr int NT = WM * WN * 64;
-    static constexpr int GPR = kBK / 32;                  // code groups per row per k step
+    static constexpr int GPR = KB / 32;                   // code groups per row per k step
     static constexpr int GROUPS = (BM + BN) * GPR;
     static constexpr int GPT = (GROUPS + NT - 1) / NT;    // groups per thread
     static constexpr int TM = BM / WM / 32, TN = BN / WN / 32;
@@ -110,16 +142,16 @@ struct GemmTile {
     }
 
     // Main loop. FAST: the tile lies inside both matrices and K is a multiple
-    // of 128, so loads need no clamping and no masking, and their addresses
+    // of KB, so loads need no clamping and no masking, and their addresses
     // are a per-thread 32-bit offset from a workgroup-uniform base.
     template <bool FAST>
     __device__ __forceinline__ static void run(uint8_t *lds, const uint8_t *A, const uint8_t *W, int n, int N,
-                                               int K, int bm0, int bn0, v16i (&acc)[TM][TN]) {
+                                               int K, int bm0, int bn0, Acc (&acc)[TM][TN]) {
         const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
         const int wm = wv / WN, wn = wv % WN;
         const int h = lane >> 5, l32 = lane & 31;
-        const uint32_t rb = static_cast<uint32_t>(K) * BITS / 8;  // packed row bytes
-        const int nkt = (K + kBK - 1) / kBK;
+        const uint32_t rb = static_cast<uint32_t>(K) / 32 * F::kGroupB;  // packed row bytes
+        const int nkt = (K + KB - 1) / KB;
         const uint8_t *abase = A + static_cast<size_t>(bm0) * rb;
         const uint8_t *wbase = W + static_cast<size_t>(bn0) * rb;
 
@@ -134,7 +166,7 @@ struct GemmTile {
             const int r = isa[i] ? row : row - BM;
             gvalid[i] = isa[i] ? bm0 + r < n : bn0 + r < N;
             goff[i] = (gvalid[i] ? static_cast<uint32_t>(r) : 0u) * rb + F::kGroupB * part;
-            ldst[i] = row * kRowLds + 32 * part;
+            ldst[i] = row * kRowLds + GB * part;
             gk[i] = 32 * part;
         }
         auto src = [&](int i) -> const uint8_t * {
@@ -157,28 +189,34 @@ struct GemmTile {
                 if constexpr (FAST) {
                     st[i].load(src(i) + goff[i] + static_cast<uint32_t>(kt) * (GPR * F::kGroupB));
                 } else {
-                    const int k = min(kt * kBK + gk[i] - gk[i] % 32, last_group_k);
+                    const int k = min(kt * KB + gk[i] - gk[i] % 32, last_group_k);
                     st[i].load(src(i) + goff[i] - (gk[i] / 32) * F::kGroupB + static_cast<uint32_t>(k / 32) * F::kGroupB);
                 }
             }
         };
-        // widen groups [i0, i1) of a slot and write them to an LDS buffer
+        // widen groups [i0, i1) of a slot (fp4: as they are) and write them
+        // to an LDS buffer
         auto store_part = [&](int kt, uint8_t *buf, Group<BITS> *st, int i0, int i1) {
 #pragma unroll
             for (int i = i0; i < i1; ++i) {
-                if constexpr (!FAST) st[i].keep_if(gvalid[i] && kt * kBK + gk[i] < K);
-                v4i lo, hi;
-                st[i].widen(lo, hi);
-                v4i *dst = reinterpret_cast<v4i *>(buf + ldst[i]);
-                dst[0] = lo;
-                dst[1] = hi;
+                if constexpr (!FAST) st[i].keep_if(gvalid[i] && kt * KB + gk[i] < K);
+                if constexpr (MX) {
+                    *reinterpret_cast<v4u *>(buf + ldst[i]) = st[i].x;
+                } else {
+                    v4i lo, hi;
+                    st[i].widen(lo, hi);
+                    v4i *dst = reinterpret_cast<v4i *>(buf + ldst[i]);
+                    dst[0] = lo;
+                    dst[1] = hi;
+                }
             }
         };
 
         const int arow = (wm * (BM / WM) + l32) * kRowLds + 16 * h;
         const int wrow = (BM + wn * (BN / WN) + l32) * kRowLds + 16 * h;
-        // operands of one 32-code step, double buffered: step s + 1 is read
-        // from LDS while the matrix cores work on step s
+        // operands of one matrix-core step (32 int8 or 64 fp4 codes), double
+        // buffered: step s + 1 is read from LDS while the matrix cores work on
+        // step s
         v4i ao[2][TM], wo[2][TN];
         auto read_ops = [&](const uint8_t *lb, int s, int slot) {
 #pragma unroll
@@ -190,8 +228,19 @@ struct GemmTile {
 #pragma unroll
             for (int i = 0; i < TM; ++i)
 #pragma unroll
-                for (int j = 0; j < TN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ao[slot][i], wo[slot][j], acc[i][j], 0, 0, 0);
+                for (int j = 0; j < TN; ++j) {
+                    if constexpr (MX) {
+                        // fp4 (format 4) on both sides, block scale 2^1 (E8M0 128); an fp4
+                        // operand is the low four registers
+                        const v4i a = ao[slot][i], b = wo[slot][j];
+                        const v8i a8 = {a[0], a[1], a[2], a[3], 0, 0, 0, 0};
+                        const v8i b8 = {b[0], b[1], b[2], b[3], 0, 0, 0, 0};
+                        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, acc[i][j], 4, 4, 0, 128,
+                                                                                    0, 128);
+                    } else {
+                        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ao[slot][i], wo[slot][j], acc[i][j], 0, 0, 0);
+                    }
+                }
         };
         // issue order inside one 32-code step: multiplies alternate with the
         // LDS reads of the next step's operands
@@ -485,7 +534,7 @@ __global__ __launch_bounds__(WM * WN * 64) void qgemm_kernel(const uint8_t *__re
                                                              int32_t *__restrict__ acc_out,
                                                              const YT *__restrict__ res, int64_t ld_r) {
     using T = GemmTile<BITS, BM, BN, WM, WN, P>;
-    using F = Fmt<BITS>;
+    constexpr int SH = Fmt<BITS>::kShift;  // scale of the int8 path's sums
     constexpr int TM = T::TM, TN = T::TN;
     __shared__ __attribute__((aligned(16))) uint8_t lds[T::LDS_BYTES];
 
@@ -498,18 +547,26 @@ __global__ __launch_bounds__(WM * WN * 64) void qgemm_kernel(const uint8_t *__re
     const int bm0 = (tile % mt) * BM;
     const int bn0 = (tile / mt) * BN;
 
+    typename T::Acc accm[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) accm[i][j][v] = 0;
+
+    if (bm0 + BM <= n && bn0 + BN <= N && K % T::KB == 0)
+        T::template run<true>(lds, A, W, n, N, K, bm0, bn0, accm);
+    else
+        T::template run<false>(lds, A, W, n, N, K, bm0, bn0, accm);
+    // (the fp4 path's float32 sums are exact integers)
     v16i acc[TM][TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0;
-
-    if (bm0 + BM <= n && bn0 + BN <= N && K % kBK == 0)
-        T::template run<true>(lds, A, W, n, N, K, bm0, bn0, acc);
-    else
-        T::template run<false>(lds, A, W, n, N, K, bm0, bn0, acc);
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = static_cast<int>(accm[i][j][v]);
 
     // epilogue: lane holds channel l32 of each fragment and tokens 8(v/4) + 4h + v%4
     constexpr int OS = BN + 8;  // bf16 row stride of the output tile in LDS
@@ -551,7 +608,7 @@ __global__ __launch_bounds__(WM * WN * 64) void qgemm_kernel(const uint8_t *__re
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
                     const int tl = wm * (BM / WM) + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
-                    float val = (static_cast<float>(acc[i][j][v] >> F::kShift) * sat[i][v]) * swj;
+                    float val = (static_cast<float>(acc[i][j][v] >> SH) * sat[i][v]) * swj;
                     if (res != nullptr) val += bf16_to_f32(ot[tl * OS + cl]);
                     ot[tl * OS + cl] = to_out<uint16_t>(val);
                 }
@@ -577,7 +634,7 @@ __global__ __launch_bounds__(WM * WN * 64) void qgemm_kernel(const uint8_t *__re
             for (int v = 0; v < 16; ++v) {
                 const int tok = bm0 + wm * (BM / WM) + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
                 if (cvalid && tok < n) {
-                    const int a = acc[i][j][v] >> F::kShift;
+                    const int a = acc[i][j][v] >> SH;
                     float val = (static_cast<float>(a) * sa[tok]) * swj;
                     if (res != nullptr) val += from_out(res[static_cast<int64_t>(tok) * ld_r + ch]);
                     y[static_cast<int64_t>(tok) * ld_y + ch] = to_out<YT>(val);
@@ -607,34 +664,40 @@ template <int BITS, typename YT>
 hipError_t launch_b(const uint8_t *a, const float *sa, int64_t n, const uint8_t *w, const float *sw, int64_t N,
                     int64_t K, void *y, int64_t ld_y, int32_t *acc_out, const void *res, int64_t ld_r, hipStream_t s) {
     const int64_t cus = device_cus();
-    // decode-size batches stream the weights once
-    const int64_t gemv_wgs = (N + 31) / 32;
-    // up to 16 tokens, or up to 64 while 16-channel workgroups fit the CUs in
-    // one round: 16-channel workgroups on the 16 x 16 x 64 matrix core (more
-    // workgroups streaming the weights; measured faster than the kernels
-    // below for 1 and 8 tokens on every layer shape and for 64 tokens at
-    // N = 4096; slower at 64 tokens for N = 12288 and 22016, where every
-    // workgroup re-reads all 64 activation rows)
-    if (n <= 16 || (n <= 64 && N / 16 <= cus)) {
-        const bool deep = K >= 8192;
-        switch ((n + 15) / 16) {
-        case 1: return deep ? launch_gemv16<BITS, 1, 8, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s)
-                            : launch_gemv16<BITS, 1, 4, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s);
-        case 2: return deep ? launch_gemv16<BITS, 2, 8, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s)
-                            : launch_gemv16<BITS, 2, 4, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s);
-        case 3: return deep ? launch_gemv16<BITS, 3, 8, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s)
-                            : launch_gemv16<BITS, 3, 4, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s);
-        default: return deep ? launch_gemv16<BITS, 4, 8, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s)
-                             : launch_gemv16<BITS, 4, 4, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s);
+    if constexpr (BITS == kFp4) {
+        // the fp4 operands have no decode-size kernels of their own: narrow tiles
+        if (n <= 32) return launch_t<BITS, 32, 32, 1, 1, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s);
+        if (n <= 64) return launch_t<BITS, 64, 32, 2, 1, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s);
+    } else {
+        // decode-size batches stream the weights once
+        const int64_t gemv_wgs = (N + 31) / 32;
+        // up to 16 tokens, or up to 64 while 16-channel workgroups fit the CUs in
+        // one round: 16-channel workgroups on the 16 x 16 x 64 matrix core (more
+        // workgroups streaming the weights; measured faster than the kernels
+        // below for 1 and 8 tokens on every layer shape and for 64 tokens at
+        // N = 4096; slower at 64 tokens for N = 12288 and 22016, where every
+        // workgroup re-reads all 64 activation rows)
+        if (n <= 16 || (n <= 64 && N / 16 <= cus)) {
+            const bool deep = K >= 8192;
+            switch ((n + 15) / 16) {
+            case 1: return deep ? launch_gemv16<BITS, 1, 8, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s)
+                                : launch_gemv16<BITS, 1, 4, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s);
+            case 2: return deep ? launch_gemv16<BITS, 2, 8, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s)
+                                : launch_gemv16<BITS, 2, 4, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s);
+            case 3: return deep ? launch_gemv16<BITS, 3, 8, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s)
+                                : launch_gemv16<BITS, 3, 4, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s);
+            default: return deep ? launch_gemv16<BITS, 4, 8, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s)
+                                 : launch_gemv16<BITS, 4, 4, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s);
+            }
         }
-    }
-    if (n <= 32) {
-        if (gemv_wgs <= 2 * cus) return launch_gemv<BITS, 1, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s);
-        return launch_t<BITS, 32, 32, 1, 1, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s);
-    }
-    if (n <= 64) {
-        if (gemv_wgs <= cus) return launch_gemv<BITS, 2, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s);
-        return launch_t<BITS, 64, 32, 2, 1, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s);
+        if (n <= 32) {
+            if (gemv_wgs <= 2 * cus) return launch_gemv<BITS, 1, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s);
+            return launch_t<BITS, 32, 32, 1, 1, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s);
+        }
+        if (n <= 64) {
+            if (gemv_wgs <= cus) return launch_gemv<BITS, 2, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s);
+            return launch_t<BITS, 64, 32, 2, 1, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s);
+        }
     }
     const int64_t mt = (n + 255) / 256;
     if (n < 256 || mt * ((N + 127) / 128) < 200)
@@ -654,11 +717,49 @@ hipError_t launch_b(const uint8_t *a, const float *sa, int64_t n, const uint8_t 
     return launch_t<BITS, 256, 128, 4, 2, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s);
 }
 
+// ------------------------------------------------- int3 codes -> fp4 codes
+// Per byte of a word: a 3-bit two's complement code u in bits 7-5 and another
+// in bits 4-2 -> two e2m1 nibbles of u / 2 (sign in bit 3, |u| in bits 1-0).
+// |u| keeps u's low bit; its second bit flips where the sign and the low bit
+// are both set (-1 -> 1, -3 -> 3, -2 -> 2).
+__device__ __forceinline__ uint32_t fp4_pair(uint32_t x) {
+    const uint32_t t = x & (x >> 2);  // sign AND low bit: bit 5 (high code), bit 2 (low code)
+    const uint32_t base = (x & 0x80808080u) | ((x >> 1) & 0x38383838u) | ((x >> 2) & 0x03030303u);
+    return base ^ ((t & 0x20202020u) | ((t >> 1) & 0x02020202u));
+}
+
+// One thread per 32-code group: 12 bytes of int3 codes (words w0, w1, w2) ->
+// 16 bytes of fp4. Word i of the output takes slots 2i (high nibbles) and
+// 2i + 1 (low nibbles); slots 6 and 7 are first gathered into the bit
+// positions of slots 0 and 1.
+__global__ __launch_bounds__(256) void codes_to_fp4_kernel(const uint32_t *__restrict__ in, v4u *__restrict__ out,
+                                                           int64_t groups) {
+    for (int64_t g = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; g < groups;
+         g += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+        const uint32_t w0 = in[3 * g], w1 = in[3 * g + 1], w2 = in[3 * g + 2];
+        const uint32_t x3 = ((w2 << 6) & 0x80808080u) | ((w0 << 5) & 0x60606060u) | ((w2 << 4) & 0x10101010u) |
+                            ((w1 << 2) & 0x0C0C0C0Cu);
+        out[g] = v4u{fp4_pair(w0), fp4_pair(w1), fp4_pair(w2), fp4_pair(x3)};
+    }
+}
+
 }  // namespace
+
+hipError_t launch_codes_to_fp4(const uint8_t *codes, int64_t rows, int64_t k, uint8_t *out, hipStream_t s) {
+    const int64_t groups = rows * (k / 32);
+    const int64_t blocks = std::min<int64_t>((groups + 255) / 256, static_cast<int64_t>(device_cus()) * 16);
+    hipLaunchKernelGGL(codes_to_fp4_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s,
+                       reinterpret_cast<const uint32_t *>(codes), reinterpret_cast<v4u *>(out), groups);
+    return hipGetLastError();
+}
 
 hipError_t launch_qgemm(const uint8_t *a, const float *sa, int64_t n, const uint8_t *w, const float *sw,
                         int64_t n_out, int64_t k, int bits, void *y, int y_dtype, int64_t ld_y,
                         int32_t *acc_out, const void *res, int64_t ld_r, hipStream_t s) {
+    if (bits == kFp4) {
+        if (y_dtype == 1) return launch_b<kFp4, uint16_t>(a, sa, n, w, sw, n_out, k, y, ld_y, acc_out, res, ld_r, s);
+        return launch_b<kFp4, float>(a, sa, n, w, sw, n_out, k, y, ld_y, acc_out, res, ld_r, s);
+    }
     if (bits == 4) {
         if (y_dtype == 1) return launch_b<4, uint16_t>(a, sa, n, w, sw, n_out, k, y, ld_y, acc_out, res, ld_r, s);
         return launch_b<4, float>(a, sa, n, w, sw, n_out, k, y, ld_y, acc_out, res, ld_r, s);

@@ -48,8 +48,15 @@ hipError_t launch_quant(const void *x, int x_dtype, int64_t n, int k, int64_t ld
                         const float *norm_w, float eps, int bits, uint8_t *codes, float *scales,
                         hipStream_t s);
 
+// Code format of launch_qgemm's operands besides packed int4 (bits 4) and
+// packed int3 (bits 3): 3-bit codes held as fp4 e2m1 nibbles.
+constexpr int kFp4 = 1;
+
+// Packed int3 rows (k codes each) -> fp4 rows (k / 2 bytes each).
+hipError_t launch_codes_to_fp4(const uint8_t *codes, int64_t rows, int64_t k, uint8_t *out, hipStream_t s);
+
 // res: NULL, or n rows of n_out values of the output type (stride ld_r) added
-// to the dequantised result before its rounding.
+// to the dequantised result before its rounding. bits: 4, 3 or kFp4.
 hipError_t launch_qgemm(const uint8_t *a, const float *sa, int64_t n, const uint8_t *w, const float *sw,
                         int64_t n_out, int64_t k, int bits, void *y, int y_dtype, int64_t ld_y,
                         int32_t *acc_out, const void *res, int64_t ld_r, hipStream_t s);

@@ -23,6 +23,12 @@ single global rotation (T = I), for the overhead comparison.
 
 Weights are quantised on the device with rsq_quant_act (per output channel,
 no norm); the sites come from ``offline.convert_site`` and rsq_site_prepare.
+
+3-bit codes at prefill sizes (more than 64 tokens) run on the fp4 matrix
+cores: the weights are converted once (rsq_codes_to_fp4) and each GEMM is
+preceded by the conversion of its activation codes, a stage of its own
+("fp4_*"), then rsq_qgemm_fp4 / its residual form; the results are the
+same bits as the int3 GEMMs'.
 """
 from __future__ import annotations
 
@@ -65,6 +71,7 @@ class QLinear:
     codes: torch.Tensor
     scales: torch.Tensor
     source: str = ""
+    fp4: torch.Tensor | None = None   # the 3-bit codes as fp4 rows, when the fp4 GEMM is used
 
 
 def make_site(U: np.ndarray, M: np.ndarray) -> Site:
@@ -110,10 +117,12 @@ class LayerPath:
     bufs: dict = field(default_factory=dict)
     mismatch: dict = field(default_factory=dict)   # site -> T (float32), kept on request
     prep_info: dict = field(default_factory=dict)  # site -> how its (U_r, M) was prepared
+    fp4: bool = False                              # 3-bit GEMMs on fp4 codes
 
     @classmethod
     def build(cls, cid: int, n: int | None = None, r: int | None = None, gqa: bool = True,
-              sites=None, weights=None, keep_mismatch: bool = False, prep: str = "host") -> "LayerPath":
+              sites=None, weights=None, keep_mismatch: bool = False, prep: str = "host",
+              fp4: bool | None = None) -> "LayerPath":
         """Device-resident inputs and outputs of one layer path.
 
         sites: optional {"A": (U, M), "B": (U, M)}; weights: optional
@@ -121,9 +130,14 @@ class LayerPath:
         keep_mismatch: also keep each synthetic site's dense T (for comparisons).
         prep: "host" (float64 eigensolver on the CPU) or "device" (float64
         block subspace iteration on the GPU) for the synthetic sites.
+        fp4: run the 3-bit GEMMs on fp4 codes; default: for 3-bit codes and
+        more than 64 tokens (the decode-size batches keep the int8 kernels).
         """
         cfg = CONFIGS[cid]
         self = cls(cfg, n or cfg.n, r or cfg.r, gqa)
+        self.fp4 = (cfg.bits == 3 and self.n > 64) if fp4 is None else bool(fp4)
+        if self.fp4 and cfg.bits != 3:
+            raise ValueError("fp4 holds 3-bit codes only")
         lins = layer_linears(cfg, gqa)
         names = sorted({l.source for l in lins if l.source.startswith("site")})
         for src in names:
@@ -162,6 +176,9 @@ class LayerPath:
                 w = np.concatenate([G.weight(cfg, part, rows, lin.K) for part, rows in lin.parts], axis=0)
             q = quantize_weight_on_device(w, cfg.bits, lin.name)
             q.source = lin.source
+            if self.fp4:
+                q.fp4 = torch.empty((q.N, q.K // 2), dtype=torch.uint8, device="cuda")
+                B.rsq_codes_to_fp4(q.codes, q.N, q.K, q.fp4)
             self.linears[lin.name] = q
             del w
         self._alloc()
@@ -169,9 +186,10 @@ class LayerPath:
 
     def clone(self) -> "LayerPath":
         """An independent copy of every device buffer (same values)."""
-        other = LayerPath(self.cfg, self.n, self.r, self.gqa, self.eps)
+        other = LayerPath(self.cfg, self.n, self.r, self.gqa, self.eps, fp4=self.fp4)
         other.sites = {k: Site(v.r, v.U.clone(), v.M.clone(), v.buf.clone()) for k, v in self.sites.items()}
-        other.linears = {k: QLinear(v.name, v.N, v.K, v.codes.clone(), v.scales.clone(), v.source)
+        other.linears = {k: QLinear(v.name, v.N, v.K, v.codes.clone(), v.scales.clone(), v.source,
+                                    None if v.fp4 is None else v.fp4.clone())
                          for k, v in self.linears.items()}
         other.bufs = {k: v.clone() for k, v in self.bufs.items()}
         return other
@@ -190,6 +208,8 @@ class LayerPath:
         for which in self.sites:
             self.bufs[f"codes_{which}"] = torch.empty((n, B.rsq_packed_row_bytes(cfg.D, bits)), dtype=torch.uint8, device="cuda")
             self.bufs[f"scales_{which}"] = torch.empty(n, dtype=torch.float32, device="cuda")
+            if self.fp4:
+                self.bufs[f"fp4_{which}"] = torch.empty((n, cfg.D // 2), dtype=torch.uint8, device="cuda")
         for name, lin in self.linears.items():
             self.bufs[f"y_{name}"] = torch.empty((n, lin.N), dtype=ydt, device="cuda")
             if lin.source in ("o_in", "down_in"):
@@ -197,6 +217,8 @@ class LayerPath:
                 self.bufs[lin.source] = _dev_bf16(x) if hdt == torch.bfloat16 else _dev(x)
                 self.bufs[f"codes_{lin.source}"] = torch.empty((n, B.rsq_packed_row_bytes(lin.K, bits)), dtype=torch.uint8, device="cuda")
                 self.bufs[f"scales_{lin.source}"] = torch.empty(n, dtype=torch.float32, device="cuda")
+                if self.fp4:
+                    self.bufs[f"fp4_{lin.source}"] = torch.empty((n, lin.K // 2), dtype=torch.uint8, device="cuda")
 
     # ------------------------------------------------------------------ run
     def stages(self, correction: bool = True, chain: bool = False):
@@ -227,7 +249,7 @@ class LayerPath:
             out.append((f"site{which}", "site" if correction else "quant", fn))
             for lin in self.linears.values():
                 if lin.source == f"site{which}":
-                    out.append(self._gemm(lin, codes, scales))
+                    out += self._gemm(lin, codes, scales, which)
                     break
             h_cur = h_out if correction else h_in
             stand_in = "o_in" if which == "A" else "down_in"
@@ -238,22 +260,28 @@ class LayerPath:
                                 lambda x=x, c=c, s=s: B.rsq_quant_act(x, c, s, bits, rmsnorm=False)))
                     if chain:
                         dst = b["h2"] if which == "A" else b["h3"]
-                        out.append(self._gemm_residual(lin, c, s, h_cur, dst))
+                        out += self._gemm(lin, c, s, stand_in, residual=h_cur, dst=dst)
                         h_cur = dst
                     else:
-                        out.append(self._gemm(lin, c, s))
+                        out += self._gemm(lin, c, s, stand_in)
         return out
 
-    def _gemm_residual(self, lin: QLinear, codes, scales, residual, dst):
-        n, bits = self.n, self.cfg.bits
-        return (f"gemm_{lin.name}_res", "gemm",
-                lambda: B.rsq_qgemm_residual(codes, scales, n, lin.codes, lin.scales, lin.N, lin.K, bits, residual, dst))
+    def _gemm(self, lin: QLinear, codes, scales, src: str, residual=None, dst=None):
+        """The stages of one linear: (the fp4 conversion of its input codes, then) the GEMM.
 
-    def _gemm(self, lin: QLinear, codes, scales):
-        y = self.bufs[f"y_{lin.name}"]
+        With a residual the result goes to dst (residual added in the epilogue)."""
         n, bits = self.n, self.cfg.bits
-        return (f"gemm_{lin.name}", "gemm",
-                lambda: B.rsq_qgemm(codes, scales, n, lin.codes, lin.scales, lin.N, lin.K, bits, y))
+        name = f"gemm_{lin.name}" + ("_res" if residual is not None else "")
+        y = dst if residual is not None else self.bufs[f"y_{lin.name}"]
+        if not self.fp4:
+            if residual is not None:
+                return [(name, "gemm", lambda: B.rsq_qgemm_residual(codes, scales, n, lin.codes, lin.scales, lin.N,
+                                                                     lin.K, bits, residual, y))]
+            return [(name, "gemm", lambda: B.rsq_qgemm(codes, scales, n, lin.codes, lin.scales, lin.N, lin.K, bits, y))]
+        a4 = self.bufs[f"fp4_{src}"]
+        return [(f"fp4_{src}", "convert", lambda: B.rsq_codes_to_fp4(codes, n, lin.K, a4)),
+                (name, "gemm", lambda: B.rsq_qgemm_fp4(a4, scales, n, lin.fp4, lin.scales, lin.N, lin.K, y,
+                                                      residual=residual))]
 
     def step(self, correction: bool = True, chain: bool = False):
         for _, _, fn in self.stages(correction, chain):
@@ -261,7 +289,7 @@ class LayerPath:
 
     def outputs(self, chain: bool = False):
         """Every tensor a step writes (for comparing two ways of running it)."""
-        keys = [k for k in self.bufs if k.startswith(("h_", "codes_", "scales_", "y_")) or k in ("h2", "h3")]
+        keys = [k for k in self.bufs if k.startswith(("h_", "codes_", "scales_", "y_", "fp4_")) or k in ("h2", "h3")]
         if chain:   # the o / down results land on the residual stream instead
             keys = [k for k in keys if k not in ("y_o", "y_down")]
         else:
@@ -295,9 +323,13 @@ class LayerPath:
         if name.startswith("quant_"):
             k = self.linears["o"].K if name == "quant_o_in" else self.linears["down"].K
             return (n * (k * hs + k * bits // 8 + 4), 0)
+        if name.startswith("fp4_"):   # int3 codes in, fp4 codes out
+            k = {"fp4_o_in": self.linears["o"].K, "fp4_down_in": self.linears["down"].K}.get(name, cfg.D)
+            return (n * (k * 3 // 8 + k // 2), 0)
         res = name.endswith("_res")
         lin = self.linears[name[len("gemm_"):len(name) - (4 if res else 0)]]
-        byts = lin.N * lin.K * bits // 8 + 4 * lin.N + n * (lin.K * bits // 8 + 4) + n * lin.N * ys
+        cb = 4 if self.fp4 else bits   # bits per stored code
+        byts = lin.N * lin.K * cb // 8 + 4 * lin.N + n * (lin.K * cb // 8 + 4) + n * lin.N * ys
         if res:
             byts += n * lin.N * hs   # the residual read beside the output write
         return (byts, 2 * n * lin.N * lin.K)

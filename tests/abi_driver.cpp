@@ -14,6 +14,7 @@ int g_launches = 0;
 hipError_t g_ret = hipSuccess;
 const void *g_res = nullptr;
 int64_t g_ld_r = -1;
+int g_bits = -1;
 int g_fail = 0, g_cases = 0;
 
 void expect(const char *what, int got, int want, int launches) {
@@ -45,10 +46,15 @@ hipError_t launch_quant(const void *, int, int64_t, int, int64_t, bool, const fl
     return g_ret;
 }
 hipError_t launch_qgemm(const uint8_t *, const float *, int64_t, const uint8_t *, const float *, int64_t, int64_t,
-                        int, void *, int, int64_t, int32_t *, const void *res, int64_t ld_r, hipStream_t) {
+                        int bits, void *, int, int64_t, int32_t *, const void *res, int64_t ld_r, hipStream_t) {
     ++g_launches;
     g_res = res;
     g_ld_r = ld_r;
+    g_bits = bits;
+    return g_ret;
+}
+hipError_t launch_codes_to_fp4(const uint8_t *, int64_t, int64_t, uint8_t *, hipStream_t) {
+    ++g_launches;
     return g_ret;
 }
 }  // namespace rsq
@@ -120,9 +126,31 @@ int main() {
     expect("residual overlap", rsq_qgemm_residual(p, f, 4, p, f, 64, 128, 4, q, 64, q + 64, RSQ_BF16, 64, nullptr), RSQ_ERR_INVALID_ARG, 0);
     expect("residual null", rsq_qgemm_residual(p, f, 4, p, f, 64, 128, 4, nullptr, 64, q, RSQ_BF16, 64, nullptr), RSQ_ERR_INVALID_ARG, 0);
 
+    // fp4 codes: conversion and the linear on them
+    expect("to_fp4 ok", rsq_codes_to_fp4(p, 4, 256, q, nullptr), RSQ_OK, 1);
+    expect("to_fp4 rows = 0", rsq_codes_to_fp4(nullptr, 0, 256, nullptr, nullptr), RSQ_OK, 0);
+    expect("to_fp4 k", rsq_codes_to_fp4(p, 4, 250, q, nullptr), RSQ_ERR_INVALID_ARG, 0);
+    expect("to_fp4 rows < 0", rsq_codes_to_fp4(p, -1, 256, q, nullptr), RSQ_ERR_INVALID_ARG, 0);
+    expect("to_fp4 overlap", rsq_codes_to_fp4(p, 4, 256, p + 256, nullptr), RSQ_ERR_INVALID_ARG, 0);
+    expect("to_fp4 misaligned", rsq_codes_to_fp4(p, 4, 256, q + 8, nullptr), RSQ_ERR_INVALID_ARG, 0);
+    expect("to_fp4 null", rsq_codes_to_fp4(p, 4, 256, nullptr, nullptr), RSQ_ERR_INVALID_ARG, 0);
+    expect("fp4 qgemm ok", rsq_qgemm_fp4(p, f, 4, p, f, 64, 128, nullptr, 0, q, RSQ_BF16, 64, nullptr, nullptr), RSQ_OK, 1);
+    if (g_bits != rsq::kFp4 || g_res != nullptr) { std::printf("FAIL fp4 qgemm: wrong code format or residual at the launcher\n"); ++g_fail; }
+    expect("fp4 qgemm residual", rsq_qgemm_fp4(p, f, 4, p, f, 64, 128, q + 65536, 64, q, RSQ_BF16, 64, nullptr, nullptr), RSQ_OK, 1);
+    if (g_res != q + 65536 || g_ld_r != 64) { std::printf("FAIL fp4 qgemm: residual not passed to the launcher\n"); ++g_fail; }
+    expect("fp4 qgemm in place", rsq_qgemm_fp4(p, f, 4, p, f, 64, 128, q, 64, q, RSQ_F32, 64, nullptr, nullptr), RSQ_OK, 1);
+    expect("fp4 qgemm in place ld", rsq_qgemm_fp4(p, f, 4, p, f, 64, 128, q, 96, q, RSQ_F32, 64, nullptr, nullptr), RSQ_ERR_INVALID_ARG, 0);
+    expect("fp4 qgemm overlap", rsq_qgemm_fp4(p, f, 4, p, f, 64, 128, q + 64, 64, q, RSQ_BF16, 64, nullptr, nullptr), RSQ_ERR_INVALID_ARG, 0);
+    expect("fp4 qgemm k max", rsq_qgemm_fp4(p, f, 4, p, f, 64, 65568, nullptr, 0, q, RSQ_BF16, 64, nullptr, nullptr), RSQ_ERR_UNSUPPORTED, 0);
+    expect("fp4 qgemm n = 0", rsq_qgemm_fp4(nullptr, nullptr, 0, nullptr, nullptr, 64, 128, nullptr, 0, nullptr, RSQ_BF16, 64, nullptr, nullptr), RSQ_OK, 0);
+    expect("fp4 qgemm acc misaligned", rsq_qgemm_fp4(p, f, 4, p, f, 64, 128, nullptr, 0, q, RSQ_BF16, 64, reinterpret_cast<int32_t *>(q + 4), nullptr), RSQ_ERR_INVALID_ARG, 0);
+    expect("qgemm int3 format", rsq_qgemm(p, f, 4, p, f, 64, 128, 3, q, RSQ_BF16, 64, nullptr, nullptr), RSQ_OK, 1);
+    if (g_bits != 3) { std::printf("FAIL int3 qgemm: wrong code format at the launcher\n"); ++g_fail; }
+
     // a launch failure surfaces as RSQ_ERR_HIP with a message; the fused call stops after the failed launch
     g_ret = hipErrorInvalidValue;
     expect("launch failure", rsq_qgemm(p, f, 4, p, f, 64, 128, 4, q, RSQ_BF16, 64, nullptr, nullptr), RSQ_ERR_HIP, 1);
+    expect("launch failure to_fp4", rsq_codes_to_fp4(p, 4, 256, q, nullptr), RSQ_ERR_HIP, 1);
     expect("launch failure fused", rsq_layer_fused(p, q, RSQ_BF16, 4, 256, p, 8, nullptr, 1e-5f, 4, q + 4096, fo + 4096, p, f, 64, q + 8192, RSQ_BF16, nullptr), RSQ_ERR_HIP, 1);
     g_ret = hipSuccess;
 

@@ -62,8 +62,10 @@ def check_site(h, U, M, dtype, bits, out, codes, scales):
     return hp, q_gpu, s_gpu
 
 
-def gemm_sampled(bits, n, N, K, seed, rows=None, cols=None, y_dtype="bf16"):
-    """Full-size GEMM on the GPU from random codes; the oracle checks sampled rows x columns."""
+def gemm_sampled(bits, n, N, K, seed, rows=None, cols=None, y_dtype="bf16", fp4=False):
+    """Full-size GEMM on the GPU from random codes; the oracle checks sampled rows x columns.
+
+    fp4: 3-bit codes converted to fp4 on the device and multiplied by rsq_qgemm_fp4."""
     import torch
     rsq = lib()
     rng = np.random.default_rng(seed)
@@ -79,8 +81,15 @@ def gemm_sampled(bits, n, N, K, seed, rows=None, cols=None, y_dtype="bf16"):
     sw = rng.uniform(1e-3, 1e-2, N).astype(np.float32)
     y = torch.empty((n, N), dtype=torch.bfloat16 if y_dtype == "bf16" else torch.float32, device="cuda")
     acc = torch.empty((n, N), dtype=torch.int32, device="cuda")
-    rsq.rsq_qgemm(torch.from_numpy(a_bytes).cuda(), to_dev(sa, "f32"), n, torch.from_numpy(w_bytes).cuda(),
-                  to_dev(sw, "f32"), N, K, bits, y, acc_out=acc)
+    if fp4:
+        a4 = torch.empty((n, K // 2), dtype=torch.uint8, device="cuda")
+        w4 = torch.empty((N, K // 2), dtype=torch.uint8, device="cuda")
+        rsq.rsq_codes_to_fp4(torch.from_numpy(a_bytes).cuda(), n, K, a4)
+        rsq.rsq_codes_to_fp4(torch.from_numpy(w_bytes).cuda(), N, K, w4)
+        rsq.rsq_qgemm_fp4(a4, to_dev(sa, "f32"), n, w4, to_dev(sw, "f32"), N, K, y, acc_out=acc)
+    else:
+        rsq.rsq_qgemm(torch.from_numpy(a_bytes).cuda(), to_dev(sa, "f32"), n, torch.from_numpy(w_bytes).cuda(),
+                      to_dev(sw, "f32"), N, K, bits, y, acc_out=acc)
     torch.cuda.synchronize()
     rows = rows if rows is not None else np.unique(np.r_[0, rng.choice(n, min(n, 96), replace=False), n - 1])
     cols = cols if cols is not None else np.unique(np.r_[0, rng.choice(N, min(N, 384), replace=False), N - 1])
@@ -92,7 +101,8 @@ def gemm_sampled(bits, n, N, K, seed, rows=None, cols=None, y_dtype="bf16"):
     y_ref = online.dequant(acc_ref, sa[rows], sw[cols], y_dtype)
     y_gpu = to_host(y[torch.from_numpy(rows).cuda()][:, torch.from_numpy(cols).cuda()])
     assert np.array_equal(np.asarray(y_gpu, np.float64), np.asarray(y_ref, np.float64))
-    print(f"  gemm bits={bits} n={n} N={N} K={K}: {len(rows)}x{len(cols)} sampled outputs bit-exact", flush=True)
+    print(f"  gemm bits={bits}{' fp4' if fp4 else ''} n={n} N={N} K={K}: {len(rows)}x{len(cols)} sampled outputs bit-exact",
+          flush=True)
 
 
 # ------------------------------------------------------------------ config 1
@@ -229,10 +239,43 @@ def test_dense_comparator_against_oracle():
     assert abs(err_gpu - err_oracle) < 5e-3
 
 
+@pytest.mark.parametrize("fp4", [False, True])
 @pytest.mark.parametrize("name,N,K", [("qkv_gqa", 6144, 4096), ("gate_up", 28672, 4096), ("down", 4096, 14336)])
-def test_config4_w3a3_gemms_full_size(name, N, K):
-    print(f"case config4 gemm {name}", flush=True)
-    gemm_sampled(3, 4096, N, K, seed=N + K + 4)
+def test_config4_w3a3_gemms_full_size(name, N, K, fp4):
+    print(f"case config4 gemm {name} fp4={fp4}", flush=True)
+    gemm_sampled(3, 4096, N, K, seed=N + K + 4, fp4=fp4)
+
+
+def test_config4_layer_on_fp4_codes_equals_the_int3_layer():
+    """The W3A3 layer (chained, 320 tokens) with its GEMMs on fp4 codes writes the
+    same bits as with the int3 GEMMs (themselves checked against the oracle), and
+    its fp4 code buffers are the oracle's fp4 packing of the int3 codes."""
+    import torch
+    from rotation_bit_post_amd.path import LayerPath
+    cfg = synth.CONFIGS[4]
+    print("case config4 layer fp4 vs int3", flush=True)
+    ua, ma, _ = oracle_site(4, "A", cfg.r)
+    ub, mb, _ = oracle_site(4, "B", cfg.r)
+    sites = {"A": (ua, ma), "B": (ub, mb)}
+    p4 = LayerPath.build(4, n=320, sites=sites)
+    p3 = LayerPath.build(4, n=320, sites=sites, fp4=False)
+    assert p4.fp4 and not p3.fp4
+    assert any(nm.startswith("fp4_") for nm, _, _ in p4.stages(chain=True))
+    for chain in (False, True):
+        p4.step(chain=chain)
+        p3.step(chain=chain)
+        torch.cuda.synchronize()
+        o4, o3 = p4.outputs(chain=chain), p3.outputs(chain=chain)
+        common = [k for k in o3 if k in o4]
+        assert len(common) == len(o3)
+        bad = [k for k in common if not torch.equal(o4[k], o3[k])]
+        assert not bad, (chain, bad)
+    for key, k in (("A", cfg.D), ("B", cfg.D), ("o_in", p4.linears["o"].K), ("down_in", p4.linears["down"].K)):
+        q = packing.unpack(p4.bufs[f"codes_{key}"].cpu().numpy(), k, 3)
+        assert np.array_equal(p4.bufs[f"fp4_{key}"].cpu().numpy(), packing.pack_fp4(q)), key
+    for name, lin in p4.linears.items():
+        q = packing.unpack(lin.codes.cpu().numpy(), lin.K, 3)
+        assert np.array_equal(lin.fp4.cpu().numpy(), packing.pack_fp4(q)), name
 
 
 # ------------------------------------------------------------------ config 5

@@ -337,6 +337,82 @@ def test_qgemm_residual_matches_oracle(bits, n, N, K, ydt, inplace):
     assert np.array_equal(np.asarray(got, np.float64), np.asarray(y_ref, np.float64))
 
 
+@pytest.mark.parametrize("rows,k", [(1, 32), (7, 224), (300, 4096), (3, 65536)])
+def test_codes_to_fp4_matches_oracle(rows, k):
+    """int3 rows -> fp4 rows, byte for byte the oracle's fp4 packing of the same codes."""
+    rsq = lib()
+    import torch
+    print(f"case codes_to_fp4 rows={rows} k={k}", flush=True)
+    codes = _random_codes(rows, k, 3, np.random.default_rng(rows + k))
+    out = torch.full((rows, k // 2), 0x5A, dtype=torch.uint8, device="cuda")
+    rsq.rsq_codes_to_fp4(torch.from_numpy(packing.pack(codes, 3)).cuda(), rows, k, out)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy(), packing.pack_fp4(codes))
+
+
+FP4_GEMM_CASES = [  # n, N, K, y dtype, residual ("none", "separate", "inplace")
+    (1, 32, 32, "f32", "none"), (20, 96, 224, "bf16", "none"), (64, 256, 4096, "bf16", "separate"),
+    (65, 288, 4096, "bf16", "none"), (200, 160, 1056, "f32", "none"), (300, 4096, 512, "bf16", "separate"),
+    (130, 256, 4096, "f32", "inplace"), (300, 256, 65536, "bf16", "none"),
+    # 256-token tiles: 256 x 256 (ragged in tokens, channels and k) and 256 x 192
+    (2000, 22048, 1056, "bf16", "none"), (1800, 12224, 4096, "bf16", "inplace"),
+]
+
+
+@pytest.mark.parametrize("n,N,K,ydt,resmode", FP4_GEMM_CASES)
+def test_qgemm_fp4_bit_exact(n, N, K, ydt, resmode):
+    """The fp4 linear equals the oracle's integer GEMM and dequantisation, and the int3 kernels' output."""
+    rsq = lib()
+    import torch
+    print(f"case qgemm_fp4 n={n} N={N} K={K} y={ydt} residual={resmode}", flush=True)
+    rng = np.random.default_rng(3 * n + N + K)
+    qa, qw = _random_codes(n, K, 3, rng), _random_codes(N, K, 3, rng)
+    if K == 65536:                        # the largest sums the codes allow, both signs
+        qa[0], qw[0], qw[1] = -3, -3, 3
+    sa = rng.uniform(0.01, 2.0, n).astype(np.float32)
+    sw = rng.uniform(1e-3, 1e-2, N).astype(np.float32)
+    tdt = torch.bfloat16 if ydt == "bf16" else torch.float32
+    a3 = torch.from_numpy(packing.pack(qa, 3)).cuda()
+    w3 = torch.from_numpy(packing.pack(qw, 3)).cuda()
+    a4 = torch.empty((n, K // 2), dtype=torch.uint8, device="cuda")
+    w4 = torch.empty((N, K // 2), dtype=torch.uint8, device="cuda")
+    rsq.rsq_codes_to_fp4(a3, n, K, a4)
+    rsq.rsq_codes_to_fp4(w3, N, K, w4)
+    sa_d, sw_d = to_dev(sa, "f32"), to_dev(sw, "f32")
+    res = None
+    if resmode != "none":
+        res = (rng.standard_normal((n, N)) * 3).astype(np.float32)
+        if ydt == "bf16":
+            res = round_to_bf16(res).astype(np.float32)
+    if resmode == "inplace":
+        y = to_dev(res, ydt)
+        rsq.rsq_qgemm_fp4(a4, sa_d, n, w4, sw_d, N, K, y, residual=y)
+    elif resmode == "separate":
+        r_dev = to_dev(res, ydt)
+        y = torch.empty((n, N), dtype=tdt, device="cuda")
+        rsq.rsq_qgemm_fp4(a4, sa_d, n, w4, sw_d, N, K, y, residual=r_dev)
+    else:
+        y = torch.empty((n, N), dtype=tdt, device="cuda")
+        acc = torch.empty((n, N), dtype=torch.int32, device="cuda")
+        rsq.rsq_qgemm_fp4(a4, sa_d, n, w4, sw_d, N, K, y, acc_out=acc)
+    torch.cuda.synchronize()
+    rows = np.arange(n) if n * N <= 4_000_000 else np.unique(np.r_[0, n - 1, rng.choice(n, 48, replace=False)])
+    acc_ref = online.gemm(qa[rows], qw)
+    if resmode == "none":
+        assert np.array_equal(acc.cpu().numpy()[rows].astype(np.int64), acc_ref)
+        y_ref = online.dequant(acc_ref, sa[rows], sw, ydt)
+    else:
+        y_ref = online.dequant_add(acc_ref, sa[rows], sw, res[rows], ydt)
+    got = to_host(y[torch.from_numpy(rows).cuda()])
+    assert np.array_equal(np.asarray(got, np.float64), np.asarray(y_ref, np.float64))
+    if resmode == "none":
+        # the int3 kernels on the same codes give the same bits
+        y3 = torch.empty_like(y)
+        rsq.rsq_qgemm(a3, sa_d, n, w3, sw_d, N, K, 3, y3)
+        torch.cuda.synchronize()
+        assert torch.equal(y, y3)
+
+
 def test_qgemm_strided_output_and_minimum_codes():
     rsq = lib()
     import torch

@@ -90,3 +90,27 @@ def test_rmsnorm_missing_eps_is_caught(monkeypatch):
 def test_dequant_missing_weight_scale_is_caught(monkeypatch):
     monkeypatch.setattr(online, "dequant", lambda acc, sa, sw, dt: (np.asarray(acc).astype(np.float32) * np.asarray(sa, np.float32)[:, None]))
     _expect_failure(T_on.test_dequant_equals_scaled_float64_sum)
+
+
+def test_fp4_mistakes_are_caught(monkeypatch):
+    real_pack, real_value = packing.pack_fp4, packing.e2m1_value
+    # nibbles of a byte swapped
+    monkeypatch.setattr(packing, "pack_fp4", lambda c: (lambda p: ((p << 4) | (p >> 4)).astype(np.uint8))(real_pack(c)))
+    _expect_failure(T_on.test_fp4_packing_hand_worked_bytes)
+    monkeypatch.setattr(packing, "pack_fp4", real_pack)
+    # exponent bias 0 instead of 1 (every normal value doubled)
+    monkeypatch.setattr(packing, "e2m1_value",
+                        lambda n: real_value(n) * (2.0 if (n >> 1) & 3 else 1.0))
+    _expect_failure(T_on.test_e2m1_values_match_the_mx_table)
+    # codes stored as plain two's complement nibbles
+    monkeypatch.setattr(packing, "e2m1_value", real_value)
+
+    def twos(c):
+        c = np.atleast_2d(np.asarray(c, np.int64))
+        out = np.zeros((c.shape[0], c.shape[1] // 2), np.int64)
+        for i in range(4):
+            for b in range(4):
+                out[:, 16 * np.arange(c.shape[1] // 32) + 4 * i + b] = ((c[:, 8 * i + b::32] & 15) << 4) | (c[:, 8 * i + 4 + b::32] & 15)
+        return out.astype(np.uint8)
+    monkeypatch.setattr(packing, "pack_fp4", twos)
+    _expect_failure(T_on.test_fp4_packing_hand_worked_bytes)

@@ -394,3 +394,62 @@ def test_layer_chain_carries_each_residual_add_into_the_next_site():
     assert np.array_equal(out["h2"], h2)
     assert np.array_equal(out["siteB"]["h_out"], h2)
     assert np.array_equal(out["h3"], round_to_bf16(d_y.astype(np.float32) + h2.astype(np.float32)))
+
+
+# ------------------------------------------------------------ fp4 codes
+def _fp4_fixture():
+    values, rows = {}, []
+    with open(os.path.join(GOLDEN, "fp4_bytes.txt")) as fh:
+        text = fh.read()
+    for line in text.splitlines():
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        left, right = (x.strip() for x in line.split("|"))
+        if "=" not in left:
+            values[int(left, 16)] = float(right)
+            continue
+        codes = np.zeros((1, 32), np.int64)
+        for item in left.split(","):
+            idx, val = item.split("=")
+            if idx == "all":
+                codes[:] = int(val)
+            else:
+                codes[0, int(idx)] = int(val)
+        rows.append((codes, [int(b, 16) for b in right.split()]))
+    return values, rows
+
+
+def test_e2m1_values_match_the_mx_table():
+    values, _ = _fp4_fixture()
+    assert sorted(values) == list(range(8))
+    for pat, v in values.items():
+        assert packing.e2m1_value(pat) == v
+        assert packing.e2m1_value(pat | 8) == -v
+
+
+def test_fp4_packing_hand_worked_bytes():
+    _, rows = _fp4_fixture()
+    assert len(rows) >= 5
+    for codes, expect in rows:
+        got = packing.pack_fp4(codes)[0]
+        assert got.tolist() == expect, codes
+        assert np.array_equal(packing.unpack_fp4(got[None, :], 32), codes)
+
+
+def test_fp4_round_trip_and_same_codes_as_int3():
+    rng = np.random.default_rng(44)
+    codes = rng.integers(-3, 4, size=(9, 160))
+    p = packing.pack_fp4(codes)
+    assert p.shape == (9, 80)
+    assert np.array_equal(packing.unpack_fp4(p, 160), codes)
+    assert np.array_equal(packing.unpack(packing.pack(codes, 3), 160, 3), packing.unpack_fp4(p, 160))
+    # every code is exact: twice the element value is the code
+    assert all(2 * packing.e2m1_value(packing.pack_fp4(np.full((1, 32), c))[0, 0] >> 4) == c for c in range(-3, 4))
+
+
+def test_fp4_rejects_codes_outside_the_3bit_range():
+    with pytest.raises(ValueError):
+        packing.pack_fp4(np.full((1, 32), -4))
+    with pytest.raises(ValueError):
+        packing.unpack_fp4(np.full((1, 16), 0x44, np.uint8), 32)   # 2.0 -> code 4
