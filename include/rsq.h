@@ -29,13 +29,13 @@
  *              slots 1,3,5: bits 2-4 of lane b of word (j-1)/2;
  *              slot 6: u bits 0-1 -> bits 0-1 of lane b of w0, u bit 2 -> bit 1 of lane b of w2;
  *              slot 7: u bits 0-1 -> bits 0-1 of lane b of w1, u bit 2 -> bit 0 of lane b of w2.
- *  - fp4 codes (rsq_codes_to_fp4, rsq_qgemm_fp4): 3-bit codes c in [-3, 3]
+ *  - fp4 codes (rsq_codes_to_fp4, rsq_qgemm_fp4, bits = 3 | RSQ_FP4): 3-bit codes c in [-3, 3]
  *    held as OCP MX fp4 (e2m1) values c / 2, one nibble each (bit 3 the sign,
  *    bits 0-1 |c|, bit 2 zero), k / 2 bytes per row; each group of 32 codes
  *    (the int3 group above) takes 16 bytes: byte 4i + b (i, b < 4) holds
  *    code 8i + b in bits 4-7 and code 8i + 4 + b in bits 0-3.
  *  - Sizes: d and k multiples of 32; n_out a multiple of 32; n >= 0 (n = 0
- *    enqueues nothing); 1 <= r <= 64; bits 3 or 4. Upper limits (beyond
+ *    enqueues nothing); 1 <= r <= 64; bits 3 or 4 (or 3 | RSQ_FP4, below). Upper limits (beyond
  *    them RSQ_ERR_UNSUPPORTED): k <= 65536 for the GEMMs (the int32
  *    accumulator bound), k <= 32768 for rsq_quant_act (one row in the
  *    registers of at most four waves); for the correction d / 32 must split
@@ -65,6 +65,12 @@ typedef enum { RSQ_F32 = 0, RSQ_BF16 = 1 } rsq_dtype;
 /* rsq_quant_act flags */
 #define RSQ_QA_RMSNORM 1u
 
+/* OR'ed into bits = 3 (bits = 3 | RSQ_FP4): the 3-bit codes are read or
+ * written in the fp4 layout instead of the packed int3 one (rsq_quant_act,
+ * rsq_correct_quant, rsq_layer_fused, rsq_qgemm, rsq_qgemm_residual;
+ * rsq_packed_row_bytes gives k / 2). */
+#define RSQ_FP4 0x100
+
 #define RSQ_MAX_RANK 64
 
 /* Library version (major*10000 + minor*100 + patch). */
@@ -74,7 +80,8 @@ const char *rsq_status_str(int status);
 /* Message of the calling thread's last failed call ("" if none). */
 const char *rsq_last_error(void);
 
-/* Bytes of one packed row of k codes (0 if k or bits is invalid). */
+/* Bytes of one packed row of k codes (0 if k or bits is invalid; bits 3,
+ * 4 or 3 | RSQ_FP4). */
 size_t rsq_packed_row_bytes(int64_t k, int bits);
 
 /*
@@ -113,7 +120,7 @@ rsq_status rsq_subspace_correct(const void *h_in, void *h_out, int h_dtype,
  *           order is the kernel's)
  *   a     = (x * inv) * w    (float32; w = norm_w, or 1 if norm_w is NULL);
  *           without the flag a = x
- *   s     = max_k |a| / qmax                           (qmax = 2^(bits-1) - 1)
+ *   s     = max_k |a| / qmax                           (qmax = 7 for bits 4, 3 for 3-bit codes)
  *   q     = clamp(rint(a / s), -qmax, qmax)             (float32 quotient, ties to even)
  *   a zero row gives s = 0 and q = 0.
  * x: n rows of k elements (x_dtype), stride ld_x. codes: n rows of

@@ -8,7 +8,7 @@ Importing it fails if the library has not been built.
 """
 from ._binding import (  # noqa: F401
     LIB, LIB_PATH, EXPORTS, RsqError,
-    RSQ_F32, RSQ_BF16, RSQ_QA_RMSNORM, RSQ_MAX_RANK,
+    RSQ_F32, RSQ_BF16, RSQ_QA_RMSNORM, RSQ_MAX_RANK, RSQ_FP4,
     rsq_version, rsq_packed_row_bytes, rsq_site_bytes, rsq_site_prepare,
     rsq_subspace_correct, rsq_quant_act, rsq_correct_quant, rsq_qgemm, rsq_qgemm_residual, rsq_layer_fused,
     rsq_codes_to_fp4, rsq_qgemm_fp4,

@@ -16,6 +16,7 @@ LIB_PATH = os.path.join(_HERE, "librsq.so")
 RSQ_OK, RSQ_ERR_INVALID_ARG, RSQ_ERR_UNSUPPORTED, RSQ_ERR_WORKSPACE, RSQ_ERR_HIP = range(5)
 RSQ_F32, RSQ_BF16 = 0, 1
 RSQ_QA_RMSNORM = 1
+RSQ_FP4 = 0x100          # bits = 3 | RSQ_FP4: 3-bit codes in the fp4 layout
 RSQ_MAX_RANK = 64
 
 

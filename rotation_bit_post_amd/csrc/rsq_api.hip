@@ -47,9 +47,13 @@ rsq_status check_site(int64_t d, int r) {
 }
 
 rsq_status check_bits(int bits) {
-    RSQ_CHECK(bits == 3 || bits == 4, RSQ_ERR_INVALID_ARG, "bits = %d must be 3 or 4", bits);
+    RSQ_CHECK(bits == 3 || bits == 4 || bits == (3 | RSQ_FP4), RSQ_ERR_INVALID_ARG,
+              "bits = %d must be 3, 4 or 3 | RSQ_FP4", bits);
     return RSQ_OK;
 }
+
+// The launchers' code format for a checked `bits`.
+int code_format(int bits) { return bits == (3 | RSQ_FP4) ? rsq::kFp4 : bits; }
 
 rsq_status check_correct_args(const void *h_in, const void *h_out, int h_dtype, int64_t n, int64_t d, int64_t ld_h,
                               const void *site, int r) {
@@ -144,7 +148,7 @@ const char *rsq_last_error(void) { return g_last_error; }
 
 size_t rsq_packed_row_bytes(int64_t k, int bits) {
     if (k <= 0 || k % 32) return 0;
-    if (bits == 4) return static_cast<size_t>(k) / 2;
+    if (bits == 4 || bits == (3 | RSQ_FP4)) return static_cast<size_t>(k) / 2;
     if (bits == 3) return static_cast<size_t>(k) * 3 / 8;
     return 0;
 }
@@ -190,7 +194,7 @@ rsq_status rsq_quant_act(const void *x, int x_dtype, int64_t n, int64_t k, int64
     if (st != RSQ_OK || n == 0) return st;
     RSQ_CHECK(x != nullptr && aligned16(x), RSQ_ERR_INVALID_ARG, "x must be non-null and 16-byte aligned");
     return hip_status(rsq::launch_quant(x, x_dtype, n, static_cast<int>(k), ld_x, (flags & RSQ_QA_RMSNORM) != 0,
-                                        norm_w, eps, bits, codes, scales, static_cast<hipStream_t>(stream)),
+                                        norm_w, eps, code_format(bits), codes, scales, static_cast<hipStream_t>(stream)),
                       "rsq_quant_act launch");
 }
 
@@ -204,7 +208,7 @@ rsq_status rsq_correct_quant(const void *h_in, void *h_out, int h_dtype, int64_t
     st = check_quant_out(n, d, bits, codes, scales);
     if (st != RSQ_OK || n == 0) return st;
     return hip_status(rsq::launch_correct(h_in, h_out, h_dtype, n, static_cast<int>(d), d, site, r, true, norm_w,
-                                          eps, bits, codes, scales, static_cast<hipStream_t>(stream)),
+                                          eps, code_format(bits), codes, scales, static_cast<hipStream_t>(stream)),
                       "rsq_correct_quant launch");
 }
 
@@ -217,8 +221,8 @@ rsq_status rsq_qgemm(const uint8_t *a_codes, const float *a_scales, int64_t n, c
     st = check_gemm(n, n_out, k, y_dtype, ld_y, a_codes, a_scales, w_codes, w_scales, y);
     if (st != RSQ_OK || n == 0) return st;
     RSQ_CHECK(acc_out == nullptr || aligned16(acc_out), RSQ_ERR_INVALID_ARG, "acc_out must be 16-byte aligned");
-    return hip_status(rsq::launch_qgemm(a_codes, a_scales, n, w_codes, w_scales, n_out, k, bits, y, y_dtype, ld_y,
-                                        acc_out, nullptr, 0, static_cast<hipStream_t>(stream)),
+    return hip_status(rsq::launch_qgemm(a_codes, a_scales, n, w_codes, w_scales, n_out, k, code_format(bits), y,
+                                        y_dtype, ld_y, acc_out, nullptr, 0, static_cast<hipStream_t>(stream)),
                       "rsq_qgemm launch");
 }
 
@@ -232,8 +236,8 @@ rsq_status rsq_qgemm_residual(const uint8_t *a_codes, const float *a_scales, int
     if (st != RSQ_OK) return st;
     st = check_residual(n, n_out, y_dtype, residual, ld_r, y, ld_y);
     if (st != RSQ_OK || n == 0) return st;
-    return hip_status(rsq::launch_qgemm(a_codes, a_scales, n, w_codes, w_scales, n_out, k, bits, y, y_dtype, ld_y,
-                                        nullptr, residual, ld_r, static_cast<hipStream_t>(stream)),
+    return hip_status(rsq::launch_qgemm(a_codes, a_scales, n, w_codes, w_scales, n_out, k, code_format(bits), y,
+                                        y_dtype, ld_y, nullptr, residual, ld_r, static_cast<hipStream_t>(stream)),
                       "rsq_qgemm_residual launch");
 }
 
@@ -289,11 +293,11 @@ rsq_status rsq_layer_fused(const void *h_in, void *h_out, int h_dtype, int64_t n
     RSQ_CHECK(aligned16(w_codes) && aligned16(w_scales) && aligned16(y), RSQ_ERR_INVALID_ARG, "operands must be 16-byte aligned");
     hipStream_t s = static_cast<hipStream_t>(stream);
     st = hip_status(rsq::launch_correct(h_in, h_out, h_dtype, n, static_cast<int>(d), d, site, r, true, norm_w, eps,
-                                        bits, codes, scales, s),
+                                        code_format(bits), codes, scales, s),
                     "rsq_layer_fused correction launch");
     if (st != RSQ_OK) return st;
-    return hip_status(rsq::launch_qgemm(codes, scales, n, w_codes, w_scales, n_out, d, bits, y, y_dtype, n_out,
-                                        nullptr, nullptr, 0, s),
+    return hip_status(rsq::launch_qgemm(codes, scales, n, w_codes, w_scales, n_out, d, code_format(bits), y, y_dtype,
+                                        n_out, nullptr, nullptr, 0, s),
                       "rsq_layer_fused GEMM launch");
 }
 

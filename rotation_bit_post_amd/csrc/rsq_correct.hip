@@ -419,10 +419,10 @@ __global__ __launch_bounds__(64 * kMaxWaves) void correct_kernel(
         for (int m = 0; m < NC; ++m) hr[m].opaque();
         const float *nw_q = norm_w;
         asm volatile("" : "+s"(nw_q));  // reload the weights below instead of keeping them live
-        const int qmax = (1 << (bits - 1)) - 1;
+        const int qmax = bits == 4 ? 7 : 3;  // bits: 4, 3 or kFp4 (3-bit codes as fp4)
         const float s = __fdiv_rn(mval, static_cast<float>(qmax));
         const float inv_s = s > 0.0f ? __fdiv_rn(1.0f, s) : 0.0f;
-        const size_t rowb = bits == 4 ? static_cast<size_t>(d) / 2 : static_cast<size_t>(d) * 3 / 8;
+        const size_t rowb = bits == 3 ? static_cast<size_t>(d) * 3 / 8 : static_cast<size_t>(d) / 2;
         auto quant_chunk = [&](int m, const float *wts) {
             const int c = w + nw * (m + base);
             uint32_t u[8];
@@ -440,6 +440,8 @@ __global__ __launch_bounds__(64 * kMaxWaves) void correct_kernel(
 #pragma unroll
                 for (int e = 0; e < 8; ++e) word |= (u[e] & 0xFu) << (4 * e);
                 if (ok) *reinterpret_cast<uint32_t *>(codes + tt * rowb + 16 * c + 4 * g) = word;
+            } else if (bits == kFp4) {   // word g of the chunk's 32-code group
+                if (ok) *reinterpret_cast<uint32_t *>(codes + tt * rowb + 16 * c + 4 * g) = fp4_word(u);
             } else {
                 uint32_t own, low[3];
                 int3_lane_parts(u, own, low);

@@ -81,6 +81,19 @@ __device__ __forceinline__ uint32_t quant_bits(float a, float s, float inv_s) {
     return __float_as_uint(y + 12582912.0f);
 }
 
+// Eight 3-bit codes (the low 3 bits of u[e], two's complement) -> one word
+// of fp4 e2m1 nibbles holding code / 2 (sign in bit 3, |code| in bits 0-1):
+// code e < 4 in the high nibble of byte e, code e >= 4 in the low nibble of
+// byte e - 4. |u| keeps u's low bit; its second bit flips where the sign and
+// the low bit are both set (-1 -> 1, -3 -> 3, -2 -> 2).
+__device__ __forceinline__ uint32_t fp4_word(const uint32_t u[8]) {
+    uint32_t w = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) w |= (u[e] & 7u) << (e < 4 ? 8 * e + 4 : 8 * (e - 4));
+    const uint32_t sg = (w >> 2) & 0x11111111u;  // each nibble's sign, at its bit 0
+    return ((w & 0x33333333u) ^ ((sg & w) << 1)) | (sg << 3);
+}
+
 // int3 packing without lane-dependent control flow. Lane group g (0..3) of a
 // 32-code group holds codes 8g .. 8g+7 (code bits in the low 3 bits of u[e]),
 // i.e. slots 2g (e < 4) and 2g + 1 (e >= 4), byte lane e % 4. Slots 2g and

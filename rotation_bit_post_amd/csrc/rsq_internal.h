@@ -13,6 +13,10 @@ inline int rank_pad(int r) { return (r + 31) / 32 * 32; }
 // (parts U hi, V hi, U lo, V lo).
 inline size_t site_bytes(int64_t d, int r) { return static_cast<size_t>(d) * rank_pad(r) * 2 * 2 * 2; }
 
+// Code formats (the launchers' `bits`): packed int4 (4), packed int3 (3), and
+// 3-bit codes held as fp4 e2m1 nibbles (kFp4).
+constexpr int kFp4 = 1;
+
 // Most waves in a correction workgroup.
 constexpr int kCorrectMaxWaves = 8;
 
@@ -39,7 +43,8 @@ int device_cus();
 
 hipError_t launch_site_prepare(const float *U, const float *M, int d, int r, void *site, hipStream_t s);
 
-// h_dtype: 0 float32, 1 bfloat16. quant: also RMSNorm + quantise + pack.
+// h_dtype: 0 float32, 1 bfloat16. quant: also RMSNorm + quantise + pack
+// (bits: 4, 3 or kFp4, the format of the codes written).
 hipError_t launch_correct(const void *h_in, void *h_out, int h_dtype, int64_t n, int d, int64_t ld_h,
                           const void *site, int r, bool quant, const float *norm_w, float eps, int bits,
                           uint8_t *codes, float *scales, hipStream_t s);
@@ -47,10 +52,6 @@ hipError_t launch_correct(const void *h_in, void *h_out, int h_dtype, int64_t n,
 hipError_t launch_quant(const void *x, int x_dtype, int64_t n, int k, int64_t ld_x, bool norm,
                         const float *norm_w, float eps, int bits, uint8_t *codes, float *scales,
                         hipStream_t s);
-
-// Code format of launch_qgemm's operands besides packed int4 (bits 4) and
-// packed int3 (bits 3): 3-bit codes held as fp4 e2m1 nibbles.
-constexpr int kFp4 = 1;
 
 // Packed int3 rows (k codes each) -> fp4 rows (k / 2 bytes each).
 hipError_t launch_codes_to_fp4(const uint8_t *codes, int64_t rows, int64_t k, uint8_t *out, hipStream_t s);

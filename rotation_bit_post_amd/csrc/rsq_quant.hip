@@ -129,10 +129,10 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(const T *__restrict__ x
     }
 #pragma unroll
     for (int m = 0; m < CH; ++m) v[m].opaque();
-    const int qmax = (1 << (bits - 1)) - 1;
+    const int qmax = bits == 4 ? 7 : 3;  // bits: 4, 3 or kFp4 (3-bit codes as fp4)
     const float s = __fdiv_rn(mval, static_cast<float>(qmax));
     const float inv_s = s > 0.0f ? __fdiv_rn(1.0f, s) : 0.0f;
-    const size_t rowb = bits == 4 ? static_cast<size_t>(k) / 2 : static_cast<size_t>(k) * 3 / 8;
+    const size_t rowb = bits == 3 ? static_cast<size_t>(k) * 3 / 8 : static_cast<size_t>(k) / 2;
     uint8_t *cr = codes + (rvalid ? row : 0) * rowb;
 
     // quantise + pack; a = x (no norm), x * inv, or (x * inv) * w
@@ -157,6 +157,8 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(const T *__restrict__ x
 #pragma unroll
             for (int e = 0; e < 8; ++e) word |= (u[e] & 0xFu) << (4 * e);
             if (rvalid && c < nch) *reinterpret_cast<uint32_t *>(cr + 4 * c) = word;
+        } else if (bits == kFp4) {   // this chunk is word c % 4 of its 32-code group
+            if (rvalid && c < nch) *reinterpret_cast<uint32_t *>(cr + 4 * c) = fp4_word(u);
         } else {
             uint32_t own, low[3];
             int3_lane_parts(u, own, low);

@@ -25,10 +25,10 @@ Weights are quantised on the device with rsq_quant_act (per output channel,
 no norm); the sites come from ``offline.convert_site`` and rsq_site_prepare.
 
 3-bit codes at prefill sizes (more than 64 tokens) run on the fp4 matrix
-cores: the weights are converted once (rsq_codes_to_fp4) and each GEMM is
-preceded by the conversion of its activation codes, a stage of its own
-("fp4_*"), then rsq_qgemm_fp4 / its residual form; the results are the
-same bits as the int3 GEMMs'.
+cores: the weights are converted once (rsq_codes_to_fp4), the sites and the
+stand-in quantisations write their codes in the fp4 layout (bits = 3 |
+RSQ_FP4) and the GEMMs are rsq_qgemm_fp4 / its residual form; the results
+are the same bits as with int3 codes.
 """
 from __future__ import annotations
 
@@ -194,8 +194,13 @@ class LayerPath:
         other.bufs = {k: v.clone() for k, v in self.bufs.items()}
         return other
 
+    @property
+    def code_bits(self) -> int:
+        """The `bits` argument of the quantising entry points: the code format written."""
+        return (3 | B.RSQ_FP4) if self.fp4 else self.cfg.bits
+
     def _alloc(self):
-        cfg, n, bits = self.cfg, self.n, self.cfg.bits
+        cfg, n, bits = self.cfg, self.n, self.code_bits
         hdt = torch.bfloat16 if cfg.h_dtype == "bf16" else torch.float32
         ydt = torch.bfloat16 if cfg.y_dtype == "bf16" else torch.float32
         h = G.residual(cfg, n)
@@ -208,8 +213,6 @@ class LayerPath:
         for which in self.sites:
             self.bufs[f"codes_{which}"] = torch.empty((n, B.rsq_packed_row_bytes(cfg.D, bits)), dtype=torch.uint8, device="cuda")
             self.bufs[f"scales_{which}"] = torch.empty(n, dtype=torch.float32, device="cuda")
-            if self.fp4:
-                self.bufs[f"fp4_{which}"] = torch.empty((n, cfg.D // 2), dtype=torch.uint8, device="cuda")
         for name, lin in self.linears.items():
             self.bufs[f"y_{name}"] = torch.empty((n, lin.N), dtype=ydt, device="cuda")
             if lin.source in ("o_in", "down_in"):
@@ -217,8 +220,6 @@ class LayerPath:
                 self.bufs[lin.source] = _dev_bf16(x) if hdt == torch.bfloat16 else _dev(x)
                 self.bufs[f"codes_{lin.source}"] = torch.empty((n, B.rsq_packed_row_bytes(lin.K, bits)), dtype=torch.uint8, device="cuda")
                 self.bufs[f"scales_{lin.source}"] = torch.empty(n, dtype=torch.float32, device="cuda")
-                if self.fp4:
-                    self.bufs[f"fp4_{lin.source}"] = torch.empty((n, lin.K // 2), dtype=torch.uint8, device="cuda")
 
     # ------------------------------------------------------------------ run
     def stages(self, correction: bool = True, chain: bool = False):
@@ -230,7 +231,7 @@ class LayerPath:
         both inside the GEMM epilogue. Without it, site B reads site A's output
         and the o / down outputs are separate tensors.
         """
-        cfg, bits, b = self.cfg, self.cfg.bits, self.bufs
+        cfg, bits, b = self.cfg, self.code_bits, self.bufs
         if chain and "B" not in self.sites:
             raise ValueError("a chained layer needs both sites")
         out = []
@@ -249,7 +250,7 @@ class LayerPath:
             out.append((f"site{which}", "site" if correction else "quant", fn))
             for lin in self.linears.values():
                 if lin.source == f"site{which}":
-                    out += self._gemm(lin, codes, scales, which)
+                    out.append(self._gemm(lin, codes, scales))
                     break
             h_cur = h_out if correction else h_in
             stand_in = "o_in" if which == "A" else "down_in"
@@ -260,28 +261,24 @@ class LayerPath:
                                 lambda x=x, c=c, s=s: B.rsq_quant_act(x, c, s, bits, rmsnorm=False)))
                     if chain:
                         dst = b["h2"] if which == "A" else b["h3"]
-                        out += self._gemm(lin, c, s, stand_in, residual=h_cur, dst=dst)
+                        out.append(self._gemm(lin, c, s, residual=h_cur, dst=dst))
                         h_cur = dst
                     else:
-                        out += self._gemm(lin, c, s, stand_in)
+                        out.append(self._gemm(lin, c, s))
         return out
 
-    def _gemm(self, lin: QLinear, codes, scales, src: str, residual=None, dst=None):
-        """The stages of one linear: (the fp4 conversion of its input codes, then) the GEMM.
-
-        With a residual the result goes to dst (residual added in the epilogue)."""
+    def _gemm(self, lin: QLinear, codes, scales, residual=None, dst=None):
+        """The stage of one linear; with a residual the result goes to dst (added in the epilogue)."""
         n, bits = self.n, self.cfg.bits
         name = f"gemm_{lin.name}" + ("_res" if residual is not None else "")
         y = dst if residual is not None else self.bufs[f"y_{lin.name}"]
-        if not self.fp4:
-            if residual is not None:
-                return [(name, "gemm", lambda: B.rsq_qgemm_residual(codes, scales, n, lin.codes, lin.scales, lin.N,
-                                                                     lin.K, bits, residual, y))]
-            return [(name, "gemm", lambda: B.rsq_qgemm(codes, scales, n, lin.codes, lin.scales, lin.N, lin.K, bits, y))]
-        a4 = self.bufs[f"fp4_{src}"]
-        return [(f"fp4_{src}", "convert", lambda: B.rsq_codes_to_fp4(codes, n, lin.K, a4)),
-                (name, "gemm", lambda: B.rsq_qgemm_fp4(a4, scales, n, lin.fp4, lin.scales, lin.N, lin.K, y,
-                                                      residual=residual))]
+        if self.fp4:
+            return (name, "gemm", lambda: B.rsq_qgemm_fp4(codes, scales, n, lin.fp4, lin.scales, lin.N, lin.K, y,
+                                                         residual=residual))
+        if residual is not None:
+            return (name, "gemm", lambda: B.rsq_qgemm_residual(codes, scales, n, lin.codes, lin.scales, lin.N, lin.K,
+                                                                bits, residual, y))
+        return (name, "gemm", lambda: B.rsq_qgemm(codes, scales, n, lin.codes, lin.scales, lin.N, lin.K, bits, y))
 
     def step(self, correction: bool = True, chain: bool = False):
         for _, _, fn in self.stages(correction, chain):
@@ -289,7 +286,7 @@ class LayerPath:
 
     def outputs(self, chain: bool = False):
         """Every tensor a step writes (for comparing two ways of running it)."""
-        keys = [k for k in self.bufs if k.startswith(("h_", "codes_", "scales_", "y_", "fp4_")) or k in ("h2", "h3")]
+        keys = [k for k in self.bufs if k.startswith(("h_", "codes_", "scales_", "y_")) or k in ("h2", "h3")]
         if chain:   # the o / down results land on the residual stream instead
             keys = [k for k in keys if k not in ("y_o", "y_down")]
         else:
@@ -314,21 +311,18 @@ class LayerPath:
     # -------------------------------------------------- algorithmic work
     def stage_work(self, name: str):
         """(algorithmic bytes, algorithmic integer ops) of one stage launch."""
-        cfg, n, bits = self.cfg, self.n, self.cfg.bits
+        cfg, n = self.cfg, self.n
+        cb = 4 if self.fp4 else cfg.bits   # bits per stored code (fp4 codes take a nibble)
         hs = 2 if cfg.h_dtype == "bf16" else 4
         ys = 2 if cfg.y_dtype == "bf16" else 4
         if name.startswith("site"):
             r = self.r
-            return (n * (2 * cfg.D * hs + cfg.D * bits // 8 + 4) + 4 * cfg.D * r + 4 * r * r, 0)
+            return (n * (2 * cfg.D * hs + cfg.D * cb // 8 + 4) + 4 * cfg.D * r + 4 * r * r, 0)
         if name.startswith("quant_"):
             k = self.linears["o"].K if name == "quant_o_in" else self.linears["down"].K
-            return (n * (k * hs + k * bits // 8 + 4), 0)
-        if name.startswith("fp4_"):   # int3 codes in, fp4 codes out
-            k = {"fp4_o_in": self.linears["o"].K, "fp4_down_in": self.linears["down"].K}.get(name, cfg.D)
-            return (n * (k * 3 // 8 + k // 2), 0)
+            return (n * (k * hs + k * cb // 8 + 4), 0)
         res = name.endswith("_res")
         lin = self.linears[name[len("gemm_"):len(name) - (4 if res else 0)]]
-        cb = 4 if self.fp4 else bits   # bits per stored code
         byts = lin.N * lin.K * cb // 8 + 4 * lin.N + n * (lin.K * cb // 8 + 4) + n * lin.N * ys
         if res:
             byts += n * lin.N * hs   # the residual read beside the output write

@@ -146,6 +146,14 @@ int main() {
     expect("fp4 qgemm acc misaligned", rsq_qgemm_fp4(p, f, 4, p, f, 64, 128, nullptr, 0, q, RSQ_BF16, 64, reinterpret_cast<int32_t *>(q + 4), nullptr), RSQ_ERR_INVALID_ARG, 0);
     expect("qgemm int3 format", rsq_qgemm(p, f, 4, p, f, 64, 128, 3, q, RSQ_BF16, 64, nullptr, nullptr), RSQ_OK, 1);
     if (g_bits != 3) { std::printf("FAIL int3 qgemm: wrong code format at the launcher\n"); ++g_fail; }
+    expect("qgemm fp4 bits", rsq_qgemm(p, f, 4, p, f, 64, 128, 3 | RSQ_FP4, q, RSQ_BF16, 64, nullptr, nullptr), RSQ_OK, 1);
+    if (g_bits != rsq::kFp4) { std::printf("FAIL qgemm bits 3 | RSQ_FP4: wrong code format at the launcher\n"); ++g_fail; }
+    expect("qgemm 4 | RSQ_FP4", rsq_qgemm(p, f, 4, p, f, 64, 128, 4 | RSQ_FP4, q, RSQ_BF16, 64, nullptr, nullptr), RSQ_ERR_INVALID_ARG, 0);
+    expect("quant fp4 codes", rsq_quant_act(p, RSQ_BF16, 4, 256, 256, RSQ_QA_RMSNORM, nullptr, 1e-5f, 3 | RSQ_FP4, q, fo, nullptr), RSQ_OK, 1);
+    expect("correct_quant fp4 codes", rsq_correct_quant(p, q, RSQ_BF16, 4, 256, p, 8, nullptr, 1e-5f, 3 | RSQ_FP4, q + 4096, fo + 4096, nullptr), RSQ_OK, 1);
+    expect("layer_fused fp4", rsq_layer_fused(p, q, RSQ_BF16, 4, 256, p, 8, nullptr, 1e-5f, 3 | RSQ_FP4, q + 4096, fo + 4096, p, f, 64, q + 8192, RSQ_BF16, nullptr), RSQ_OK, 2);
+    if (g_bits != rsq::kFp4) { std::printf("FAIL layer_fused bits 3 | RSQ_FP4: wrong code format at the GEMM\n"); ++g_fail; }
+    expect("row bytes fp4", rsq_packed_row_bytes(64, 3 | RSQ_FP4) == 32 ? 0 : 1, 0, 0);
 
     // a launch failure surfaces as RSQ_ERR_HIP with a message; the fused call stops after the failed launch
     g_ret = hipErrorInvalidValue;

@@ -80,3 +80,18 @@ def code_mismatch_ok(gpu_codes, ref_codes, max_frac=1e-4):
     """Codes may differ only by one level, on at most max_frac of the elements."""
     d = np.abs(np.asarray(gpu_codes, np.int64) - np.asarray(ref_codes, np.int64))
     return int(d.max(initial=0)) <= 1 and float(np.mean(d != 0)) <= max_frac, int(np.sum(d != 0)), int(d.max(initial=0))
+
+
+def subspace_site(d, r, seed, eps=0.3):
+    """(U32, M32) with U an orthonormal d x r basis and M = Q - I for an orthogonal r x r Q.
+
+    The correction's arithmetic needs no full-width rotation behind (U, M):
+    this site is as valid an input as one from a mismatch's SVD and costs no
+    d x d solve or SVD (at d = 8192 those take minutes on the host).
+    """
+    rng = np.random.default_rng(seed)
+    u, _ = np.linalg.qr(rng.standard_normal((d, r)))
+    g = np.random.default_rng(seed + 1).standard_normal((r, r))
+    a = np.triu(g, 1)
+    q = prep.cayley(eps * (a - a.T))
+    return u.astype(np.float32), (q - np.eye(r)).astype(np.float32)

@@ -12,7 +12,8 @@ import pytest
 
 from oracle import online, packing, prep
 from oracle.numerics import round_to_bf16
-from gpu_helpers import (code_mismatch_ok, empty_f32, empty_u8, lib, rel_l2, require_gpu, to_dev, to_host)
+from gpu_helpers import (code_mismatch_ok, empty_f32, empty_u8, lib, rel_l2, require_gpu, subspace_site, to_dev,
+                         to_host)
 
 pytestmark = pytest.mark.gpu
 
@@ -33,19 +34,6 @@ def random_site(d, r, seed, eps=0.05):
     t = prep.cayley(eps * _skew(d, seed + 1)).T @ prep.cayley(eps * _skew(d, seed))
     u, _ = prep.principal_subspace(t, r)
     return u.astype(np.float32), prep.subspace_transform(t, u).astype(np.float32)
-
-
-def subspace_site(d, r, seed, eps=0.3):
-    """(U32, M32) with U an orthonormal d x r basis and M = Q - I for an orthogonal r x r Q.
-
-    The correction's arithmetic needs no full-width rotation behind (U, M):
-    this site is as valid an input as random_site's and costs no d x d
-    solve or SVD (at d = 8192 those take minutes on the host).
-    """
-    rng = np.random.default_rng(seed)
-    u, _ = np.linalg.qr(rng.standard_normal((d, r)))
-    q = prep.cayley(eps * _skew(r, seed + 1))
-    return u.astype(np.float32), (q - np.eye(r)).astype(np.float32)
 
 
 def residual(n, d, dtype, seed, outliers=3, scale=40.0):
@@ -348,6 +336,55 @@ def test_codes_to_fp4_matches_oracle(rows, k):
     rsq.rsq_codes_to_fp4(torch.from_numpy(packing.pack(codes, 3)).cuda(), rows, k, out)
     torch.cuda.synchronize()
     assert np.array_equal(out.cpu().numpy(), packing.pack_fp4(codes))
+
+
+@pytest.mark.parametrize("entry,dtype,n,d", [("quant", "bf16", 33, 4096), ("quant", "f32", 5, 11008),
+                                             ("quant_w", "bf16", 300, 1024), ("correct", "bf16", 2048, 4096),
+                                             ("correct", "bf16", 64, 4096), ("correct_w", "f32", 40, 1024),
+                                             ("fused", "bf16", 300, 4096)])
+def test_fp4_codes_written_by_the_quantisers(entry, dtype, n, d):
+    """bits = 3 | RSQ_FP4: the same codes as bits = 3 in the fp4 layout (and the same scales,
+    h_out and y), at prefill and decode sizes (the latter through the column-split correction)."""
+    rsq = lib()
+    import torch
+    print(f"case fp4 codes {entry} dtype={dtype} n={n} d={d}", flush=True)
+    fp4 = 3 | rsq.RSQ_FP4
+    assert rsq.rsq_packed_row_bytes(d, fp4) == d // 2
+    x = residual(n, d, dtype, seed=n + d)
+    if n > 2:
+        x[1] = 0.0
+    xd = to_dev(x, dtype)
+    w = to_dev(np.random.default_rng(3).uniform(0.5, 1.5, d).astype(np.float32), "f32") if entry.endswith("_w") else None
+    outs = {}
+    for bits in (3, fp4):
+        codes, scales = empty_u8(n, rsq.rsq_packed_row_bytes(d, bits)), empty_f32(n)
+        h_out = y = None
+        if entry.startswith("quant"):
+            rsq.rsq_quant_act(xd, codes, scales, bits, rmsnorm=True, norm_w=w, eps=1e-5)
+        else:
+            r = 32
+            U, M = subspace_site(d, r, seed=d) if d > 1024 else random_site(d, r, seed=d)
+            site = gpu_site(U, M)
+            h_out = torch.empty_like(xd)
+            if entry.startswith("correct"):
+                rsq.rsq_correct_quant(xd, h_out, site, r, codes, scales, bits, norm_w=w, eps=1e-5)
+            else:
+                N = 256
+                qw = np.random.default_rng(9).integers(-3, 4, (N, d))
+                wc = packing.pack(qw, 3) if bits == 3 else packing.pack_fp4(qw)
+                sw = to_dev(np.random.default_rng(10).uniform(1e-3, 1e-2, N).astype(np.float32), "f32")
+                y = torch.empty((n, N), dtype=xd.dtype, device="cuda")
+                rsq.rsq_layer_fused(xd, h_out, site, r, codes, scales, torch.from_numpy(wc).cuda(), sw, N, y, bits)
+        torch.cuda.synchronize()
+        outs[bits] = (codes.cpu().numpy(), scales.cpu().numpy(), h_out, y)
+    c3, s3, h3, y3 = outs[3]
+    c4, s4, h4, y4 = outs[fp4]
+    assert np.array_equal(c4, packing.pack_fp4(packing.unpack(c3, d, 3)))
+    assert np.array_equal(s4, s3)
+    if h3 is not None:
+        assert torch.equal(h4, h3)
+    if y3 is not None:
+        assert torch.equal(y4, y3)
 
 
 FP4_GEMM_CASES = [  # n, N, K, y dtype, residual ("none", "separate", "inplace")
