@@ -171,10 +171,12 @@ __device__ __forceinline__ v8bf load_op(const uint16_t *p) { return as_v8bf(*rei
 // each forms the whole projection (U is read through L2 by all of them) but
 // reprojects and stores only its slice of nw chunks, one per wave, so a few
 // tokens still spread over many compute units.
-template <typename T, int CPW, int R32, bool QUANT, bool COLS = false>
+// FMT: the code format written when quantising (4, 3 or kFp4), a template
+// parameter so that no instance carries the branches of the others.
+template <typename T, int CPW, int R32, bool QUANT, bool COLS = false, int FMT = 4>
 __global__ __launch_bounds__(64 * kMaxWaves) void correct_kernel(
     const T *__restrict__ h_in, T *__restrict__ h_out, int64_t n, int d, int64_t ld_h,
-    const uint16_t *__restrict__ site, int tb, const float *__restrict__ norm_w, float eps, int bits,
+    const uint16_t *__restrict__ site, int tb, const float *__restrict__ norm_w, float eps,
     uint8_t *__restrict__ codes, float *__restrict__ scales) {
     static_assert(!(COLS && QUANT), "the column-split variant does not quantise");
     constexpr bool SPLIT = Row8<T>::kSplit;
@@ -419,10 +421,10 @@ __global__ __launch_bounds__(64 * kMaxWaves) void correct_kernel(
         for (int m = 0; m < NC; ++m) hr[m].opaque();
         const float *nw_q = norm_w;
         asm volatile("" : "+s"(nw_q));  // reload the weights below instead of keeping them live
-        const int qmax = bits == 4 ? 7 : 3;  // bits: 4, 3 or kFp4 (3-bit codes as fp4)
+        constexpr int qmax = FMT == 4 ? 7 : 3;
         const float s = __fdiv_rn(mval, static_cast<float>(qmax));
         const float inv_s = s > 0.0f ? __fdiv_rn(1.0f, s) : 0.0f;
-        const size_t rowb = bits == 3 ? static_cast<size_t>(d) * 3 / 8 : static_cast<size_t>(d) / 2;
+        const size_t rowb = FMT == 3 ? static_cast<size_t>(d) * 3 / 8 : static_cast<size_t>(d) / 2;
         auto quant_chunk = [&](int m, const float *wts) {
             const int c = w + nw * (m + base);
             uint32_t u[8];
@@ -435,12 +437,12 @@ __global__ __launch_bounds__(64 * kMaxWaves) void correct_kernel(
 #pragma unroll
                 for (int e = 0; e < 8; ++e) u[e] = quant_bits(hr[m].get(e) * inv, s, inv_s);
             }
-            if (bits == 4) {
+            if constexpr (FMT == 4) {
                 uint32_t word = 0;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) word |= (u[e] & 0xFu) << (4 * e);
                 if (ok) *reinterpret_cast<uint32_t *>(codes + tt * rowb + 16 * c + 4 * g) = word;
-            } else if (bits == kFp4) {   // word g of the chunk's 32-code group
+            } else if constexpr (FMT == kFp4) {   // word g of the chunk's 32-code group
                 if (ok) *reinterpret_cast<uint32_t *>(codes + tt * rowb + 16 * c + 4 * g) = fp4_word(u);
             } else {
                 uint32_t own, low[3];
@@ -513,16 +515,29 @@ hipError_t launch_t(const void *h_in, void *h_out, int64_t n, int d, int64_t ld_
         if (h_in != h_out && blocks * CPW <= cus) {
             hipLaunchKernelGGL((correct_kernel<T, CPW, R32, false, true>), dim3(static_cast<unsigned>(blocks * CPW)),
                                dim3(64 * nw), 0, s, static_cast<const T *>(h_in), static_cast<T *>(h_out), n, d, ld_h,
-                               static_cast<const uint16_t *>(site), tb, nullptr, 0.0f, bits, nullptr, nullptr);
+                               static_cast<const uint16_t *>(site), tb, nullptr, 0.0f, nullptr, nullptr);
             hipError_t e = hipGetLastError();
             if (e != hipSuccess || !QUANT) return e;
             return launch_quant(h_out, sizeof(T) == 2 ? 1 : 0, n, d, ld_h, true, norm_w, eps, bits, codes, scales, s);
         }
     }
-    const unsigned grid = static_cast<unsigned>(blocks);
-    hipLaunchKernelGGL((correct_kernel<T, CPW, R32, QUANT>), dim3(grid), dim3(64 * nw), 0, s,
-                       static_cast<const T *>(h_in), static_cast<T *>(h_out), n, d, ld_h,
-                       static_cast<const uint16_t *>(site), tb, norm_w, eps, bits, codes, scales);
+    const dim3 grid(static_cast<unsigned>(blocks)), block(64 * nw);
+    const T *hi = static_cast<const T *>(h_in);
+    T *ho = static_cast<T *>(h_out);
+    const uint16_t *st = static_cast<const uint16_t *>(site);
+    if constexpr (!QUANT) {
+        hipLaunchKernelGGL((correct_kernel<T, CPW, R32, false>), grid, block, 0, s, hi, ho, n, d, ld_h, st, tb, norm_w,
+                           eps, codes, scales);
+    } else if (bits == 4) {
+        hipLaunchKernelGGL((correct_kernel<T, CPW, R32, true, false, 4>), grid, block, 0, s, hi, ho, n, d, ld_h, st, tb,
+                           norm_w, eps, codes, scales);
+    } else if (bits == kFp4) {
+        hipLaunchKernelGGL((correct_kernel<T, CPW, R32, true, false, kFp4>), grid, block, 0, s, hi, ho, n, d, ld_h, st,
+                           tb, norm_w, eps, codes, scales);
+    } else {
+        hipLaunchKernelGGL((correct_kernel<T, CPW, R32, true, false, 3>), grid, block, 0, s, hi, ho, n, d, ld_h, st, tb,
+                           norm_w, eps, codes, scales);
+    }
     return hipGetLastError();
 }
 

@@ -52,12 +52,13 @@ template <> struct Chunk8<float> {
     __device__ __forceinline__ void opaque() { asm volatile("" : "+v"(a), "+v"(b)); }
 };
 
-// CH: chunks per lane (compile time); WPR: waves per row.
-template <typename T, int CH, int WPR>
+// CH: chunks per lane (compile time); WPR: waves per row; FMT: code format
+// (4, 3 or kFp4), a template parameter so that no instance carries the
+// branches of the others.
+template <typename T, int CH, int WPR, int FMT>
 __global__ __launch_bounds__(kThreads) void quant_kernel(const T *__restrict__ x, int64_t n, int k, int64_t ld_x,
                                                         int norm, const float *__restrict__ norm_w, float eps,
-                                                        int bits, uint8_t *__restrict__ codes,
-                                                        float *__restrict__ scales) {
+                                                        uint8_t *__restrict__ codes, float *__restrict__ scales) {
     constexpr int RPB = 4 / WPR;  // rows per workgroup
     __shared__ double lss[4];
     __shared__ float lam[4], lwm[4];
@@ -129,10 +130,10 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(const T *__restrict__ x
     }
 #pragma unroll
     for (int m = 0; m < CH; ++m) v[m].opaque();
-    const int qmax = bits == 4 ? 7 : 3;  // bits: 4, 3 or kFp4 (3-bit codes as fp4)
+    constexpr int qmax = FMT == 4 ? 7 : 3;
     const float s = __fdiv_rn(mval, static_cast<float>(qmax));
     const float inv_s = s > 0.0f ? __fdiv_rn(1.0f, s) : 0.0f;
-    const size_t rowb = bits == 3 ? static_cast<size_t>(k) * 3 / 8 : static_cast<size_t>(k) / 2;
+    const size_t rowb = FMT == 3 ? static_cast<size_t>(k) * 3 / 8 : static_cast<size_t>(k) / 2;
     uint8_t *cr = codes + (rvalid ? row : 0) * rowb;
 
     // quantise + pack; a = x (no norm), x * inv, or (x * inv) * w
@@ -152,12 +153,12 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(const T *__restrict__ x
 #pragma unroll
             for (int e = 0; e < 8; ++e) u[e] = quant_bits(v[m].get(e), s, inv_s);
         }
-        if (bits == 4) {
+        if constexpr (FMT == 4) {
             uint32_t word = 0;
 #pragma unroll
             for (int e = 0; e < 8; ++e) word |= (u[e] & 0xFu) << (4 * e);
             if (rvalid && c < nch) *reinterpret_cast<uint32_t *>(cr + 4 * c) = word;
-        } else if (bits == kFp4) {   // this chunk is word c % 4 of its 32-code group
+        } else if constexpr (FMT == kFp4) {   // this chunk is word c % 4 of its 32-code group
             if (rvalid && c < nch) *reinterpret_cast<uint32_t *>(cr + 4 * c) = fp4_word(u);
         } else {
             uint32_t own, low[3];
@@ -187,8 +188,17 @@ template <typename T, int CH, int WPR>
 hipError_t launch_t(const void *x, int64_t n, int k, int64_t ld_x, bool norm, const float *norm_w, float eps,
                     int bits, uint8_t *codes, float *scales, hipStream_t s) {
     constexpr int RPB = 4 / WPR;
-    hipLaunchKernelGGL((quant_kernel<T, CH, WPR>), dim3(static_cast<unsigned>((n + RPB - 1) / RPB)), dim3(kThreads),
-                       0, s, static_cast<const T *>(x), n, k, ld_x, norm ? 1 : 0, norm_w, eps, bits, codes, scales);
+    const dim3 grid(static_cast<unsigned>((n + RPB - 1) / RPB));
+    const T *xt = static_cast<const T *>(x);
+    if (bits == 4)
+        hipLaunchKernelGGL((quant_kernel<T, CH, WPR, 4>), grid, dim3(kThreads), 0, s, xt, n, k, ld_x, norm ? 1 : 0,
+                           norm_w, eps, codes, scales);
+    else if (bits == kFp4)
+        hipLaunchKernelGGL((quant_kernel<T, CH, WPR, kFp4>), grid, dim3(kThreads), 0, s, xt, n, k, ld_x, norm ? 1 : 0,
+                           norm_w, eps, codes, scales);
+    else
+        hipLaunchKernelGGL((quant_kernel<T, CH, WPR, 3>), grid, dim3(kThreads), 0, s, xt, n, k, ld_x, norm ? 1 : 0,
+                           norm_w, eps, codes, scales);
     return hipGetLastError();
 }
 
