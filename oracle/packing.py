@@ -131,7 +131,8 @@ def pack_fp4(codes) -> np.ndarray:
         raise ValueError("fp4 rows need a multiple of 32 codes")
     if np.any(np.abs(c) > 3):
         raise ValueError("code out of range")
-    nib = np.vectorize(_fp4_nibble, otypes=[np.int64])(c) if c.size else c
+    table = np.array([_fp4_nibble(v) for v in range(-3, 4)], dtype=np.int64)   # code -3..3 -> pattern
+    nib = table[c + 3]
     out = np.zeros((rows, k // 2), dtype=np.int64)
     for i in range(4):
         for b in range(4):
