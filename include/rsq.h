@@ -66,9 +66,10 @@ typedef enum { RSQ_F32 = 0, RSQ_BF16 = 1 } rsq_dtype;
 #define RSQ_QA_RMSNORM 1u
 
 /* OR'ed into bits = 3 (bits = 3 | RSQ_FP4): the 3-bit codes are read or
- * written in the fp4 layout instead of the packed int3 one (rsq_quant_act,
- * rsq_correct_quant, rsq_layer_fused, rsq_qgemm, rsq_qgemm_residual;
- * rsq_packed_row_bytes gives k / 2). */
+ * written in the fp4 layout instead of the packed int3 one: the codes that
+ * rsq_quant_act, rsq_correct_quant and rsq_layer_fused write, and the
+ * activation and weight codes that rsq_qgemm, rsq_qgemm_residual and
+ * rsq_layer_fused read (rsq_packed_row_bytes gives k / 2). */
 #define RSQ_FP4 0x100
 
 #define RSQ_MAX_RANK 64

@@ -375,6 +375,34 @@ def test_layer_step_replayed_as_a_hip_graph_matches_eager():
         assert not bad, (rep, bad)
 
 
+def test_fp4_layer_step_replayed_as_a_hip_graph_matches_eager():
+    """The chained W3A3 layer on fp4 codes (codes written as fp4 by the sites and
+    stand-in quantisations, GEMMs on the fp4 matrix cores) recorded once as a HIP
+    graph: every replay, with eager work in between, reproduces the eager step."""
+    import torch
+    from rotation_bit_post_amd.path import LayerPath
+    rsq = lib()
+    cfg = synth.CONFIGS[4]
+    print("case config4 fp4 layer graph replay", flush=True)
+    sites = {"A": subspace_site(cfg.D, cfg.r, seed=43), "B": subspace_site(cfg.D, cfg.r, seed=44)}
+    path = LayerPath.build(4, n=192, sites=sites, fp4=True)
+    path.step(chain=True)
+    torch.cuda.synchronize()
+    ref = {k: v.clone() for k, v in path.outputs(chain=True).items()}
+    graph = path.capture(chain=True)
+    scratch_c = empty_u8(192, cfg.D // 2)
+    scratch_s = empty_f32(192)
+    for rep in range(3):
+        for v in path.outputs(chain=True).values():
+            v.zero_()
+        rsq.rsq_quant_act(path.bufs["h"], scratch_c, scratch_s, path.code_bits, rmsnorm=True)   # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        bad = [k for k, v in path.outputs(chain=True).items() if not torch.equal(v, ref[k])]
+        assert not bad, (rep, bad)
+
+
 def test_device_offline_prep_matches_oracle_at_full_size():
     """Site A of the LLaMA-2-7B-shaped workload prepared on the GPU (float64 block
     subspace iteration) spans the oracle's SVD subspace and acts as the same operator."""
