@@ -27,9 +27,10 @@
 // float32 accumulation is exact in any order and converts back to the same
 // int32 sums. The fp4 multiply takes 64 codes per instruction at the rate the
 // int8 one takes 32; the fp4 tiles go into LDS as loaded (half the LDS bytes
-// per code of the widened int8 tiles, no widening). Turning int3 codes into
-// fp4 costs more per code than widening them, so it is a pass of its own
-// (codes_to_fp4_kernel), once per activation matrix and once per weight.
+// per code of the widened int8 tiles, no widening). Turning packed int3 codes
+// into fp4 costs more per code than widening them, so the GEMM never does it:
+// the quantisers write activation codes as fp4, and weights are converted
+// once (codes_to_fp4_kernel).
 #include <algorithm>
 #include <type_traits>
 
@@ -242,8 +243,8 @@ struct GemmTile {
                     }
                 }
         };
-        // issue order inside one 32-code step: multiplies alternate with the
-        // LDS reads of the next step's operands
+        // issue order inside one matrix-core step: multiplies alternate with
+        // the LDS reads of the next step's operands
         auto interleave = [&]() {
 #pragma unroll
             for (int q = 0; q < TM + TN; ++q) {
