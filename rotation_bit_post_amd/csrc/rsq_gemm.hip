@@ -668,7 +668,7 @@ hipError_t launch_b(const uint8_t *a, const float *sa, int64_t n, const uint8_t 
     if constexpr (BITS == kFp4) {
         // the fp4 operands have no decode-size kernels of their own: narrow tiles
         if (n <= 32) return launch_t<BITS, 32, 32, 1, 1, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s);
-        if (n <= 64) return launch_t<BITS, 64, 32, 2, 1, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s);
+        if (n <= 64) return launch_t<BITS, 64, 64, 2, 2, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s);
     } else {
         // decode-size batches stream the weights once
         const int64_t gemv_wgs = (N + 31) / 32;
@@ -696,8 +696,10 @@ hipError_t launch_b(const uint8_t *a, const float *sa, int64_t n, const uint8_t 
             return launch_t<BITS, 32, 32, 1, 1, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s);
         }
         if (n <= 64) {
+            // 64 x 64 tiles: half the re-reads of the activation rows of 64 x 32
+            // tiles (q|k|v at 64 tokens: 13.1 against 15.2 us; gate|up equal)
             if (gemv_wgs <= cus) return launch_gemv<BITS, 2, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s);
-            return launch_t<BITS, 64, 32, 2, 1, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s);
+            return launch_t<BITS, 64, 64, 2, 2, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s);
         }
     }
     const int64_t mt = (n + 255) / 256;
