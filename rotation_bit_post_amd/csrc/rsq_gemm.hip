@@ -422,9 +422,9 @@ __global__ __launch_bounds__(NW * 64) void qgemv_kernel(const uint8_t *__restric
 // 256-code k step is split over the lane quarters: lane quarter q takes codes
 // [64q, 64q + 64) (groups 2q and 2q + 1) and matrix-core step s its 16-code
 // block s, the same order for both operands. NW waves take k steps w, w + NW,
-// ... with operands loaded straight into registers two steps ahead and sum
+// ... with operands loaded straight into registers D steps ahead and sum
 // their accumulators through LDS at the end in a fixed order.
-template <int BITS, int TB, int NW, typename YT>
+template <int BITS, int TB, int NW, typename YT, int D = 2>
 __global__ __launch_bounds__(NW * 64) void qgemv16_kernel(const uint8_t *__restrict__ A, const float *__restrict__ sa,
                                                           int n, const uint8_t *__restrict__ W,
                                                           const float *__restrict__ sw, int N, int K,
@@ -445,7 +445,7 @@ __global__ __launch_bounds__(NW * 64) void qgemv16_kernel(const uint8_t *__restr
 #pragma unroll
     for (int i = 0; i < TB; ++i) arow[i] = A + static_cast<size_t>(min(16 * i + c16, n - 1)) * rb;
 
-    Frag<BITS> fa[2][TB], fw[2];
+    Frag<BITS> fa[D][TB], fw[D];
     // groups past the row end read the row's first group (in bounds); the
     // weight operand of such a group is zeroed before use
     auto load_step = [&](int kt, int slot) {
@@ -472,13 +472,16 @@ __global__ __launch_bounds__(NW * 64) void qgemv16_kernel(const uint8_t *__restr
                 acc[i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa[slot][i].op(s), wo, acc[i], 0, 0, 0);
         }
     };
-    load_step(w, 0);
-    load_step(w + NW, 1);
-    for (int kt = w; kt < nkt; kt += 2 * NW) {
-        compute(kt, 0);
-        load_step(kt + 2 * NW, 0);
-        compute(kt + NW, 1);
-        load_step(kt + 3 * NW, 1);
+    // a ring of D register slots: slot u holds k step kt + u NW while the
+    // steps before it are multiplied (steps past the end reload the last one)
+#pragma unroll
+    for (int u = 0; u < D; ++u) load_step(w + u * NW, u);
+    for (int kt = w; kt < nkt; kt += D * NW) {
+#pragma unroll
+        for (int u = 0; u < D; ++u) {
+            compute(kt + u * NW, u);
+            load_step(kt + (u + D) * NW, u);
+        }
     }
 
     // sum the waves' partial accumulators (fixed order) and write the outputs:
@@ -505,11 +508,11 @@ __global__ __launch_bounds__(NW * 64) void qgemv16_kernel(const uint8_t *__restr
     }
 }
 
-template <int BITS, int TB, int NW, typename YT>
+template <int BITS, int TB, int NW, typename YT, int D = 2>
 hipError_t launch_gemv16(const uint8_t *a, const float *sa, int64_t n, const uint8_t *w, const float *sw, int64_t N,
                          int64_t K, void *y, int64_t ld_y, int32_t *acc_out, const void *res, int64_t ld_r,
                          hipStream_t s) {
-    hipLaunchKernelGGL((qgemv16_kernel<BITS, TB, NW, YT>), dim3(static_cast<unsigned>(N / 16)), dim3(NW * 64), 0,
+    hipLaunchKernelGGL((qgemv16_kernel<BITS, TB, NW, YT, D>), dim3(static_cast<unsigned>(N / 16)), dim3(NW * 64), 0,
                        s, a, sa, static_cast<int>(n), w, sw, static_cast<int>(N), static_cast<int>(K),
                        static_cast<YT *>(y), ld_y, acc_out, static_cast<const YT *>(res), ld_r);
     return hipGetLastError();
@@ -678,10 +681,13 @@ hipError_t launch_b(const uint8_t *a, const float *sa, int64_t n, const uint8_t 
         // below for 1 and 8 tokens on every layer shape and for 64 tokens at
         // N = 4096; slower at 64 tokens for N = 12288 and 22016, where every
         // workgroup re-reads all 64 activation rows)
+        // long k: more k steps in flight (up to 16 tokens: 4 waves with a
+        // 3-step ring, e.g. 1 token at K = 11008: 6.5 against 7.5 us for 8
+        // waves with 2; more tokens: 8 waves with 2)
         if (n <= 16 || (n <= 64 && N / 16 <= cus)) {
             const bool deep = K >= 8192;
             switch ((n + 15) / 16) {
-            case 1: return deep ? launch_gemv16<BITS, 1, 8, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s)
+            case 1: return deep ? launch_gemv16<BITS, 1, 4, YT, 3>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s)
                                 : launch_gemv16<BITS, 1, 4, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s);
             case 2: return deep ? launch_gemv16<BITS, 2, 8, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s)
                                 : launch_gemv16<BITS, 2, 4, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s);

@@ -196,6 +196,8 @@ GEMM_CASES = [  # bits, n, N, K, y dtype
     (4, 300, 4096, 512, "bf16"), (4, 20, 16448, 256, "bf16"), (3, 50, 8224, 224, "f32"),
     # 16-channel decode kernel: one token block of a wide layer, int3 with a long k, three token blocks
     (4, 16, 22016, 4096, "bf16"), (3, 12, 4096, 11008, "bf16"), (4, 40, 2048, 4128, "f32"),
+    # long k with the 3-step register ring (1 and 16 tokens, ragged last k step)
+    (4, 1, 64, 8224, "f32"), (3, 16, 128, 16416, "bf16"),
 ]
 
 
