@@ -1,6 +1,6 @@
 """Throughput of one decoder layer's linear path (ReSpinQuant online path) on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--config 2] [--copies 2] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workload llama2-7b-prefill-w4a4] [--copies 2] [--no-cpu-baseline]
 
 A step is one pass of the whole path over one batch: two correction sites
 (correction + RMSNorm + per-token quantisation), two stand-in activation
@@ -41,7 +41,8 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--config", type=int, default=2)
+    # a workload name from synth.WORKLOADS, or its position there (1-5)
+    p.add_argument("--workload", "--config", dest="workload", default="llama2-7b-prefill-w4a4")
     p.add_argument("--copies", type=int, default=2)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample", type=int, default=2048,
@@ -121,16 +122,16 @@ def dense_comparator(path, which: str = "A", iters: int = 20):
     }
 
 
-def rank_sweep(cid: int, iters: int = 20):
+def rank_sweep(wl, iters: int = 20):
     """Correction time and distance from dense h T at every rank of the workload."""
     import torch
     import rotation_bit_post_amd as B
     from rotation_bit_post_amd import offline
     from rotation_bit_post_amd.path import make_site, synthetic_mismatch
     import synth
-    cfg = synth.CONFIGS[cid]
+    cfg = synth.workload(wl)
     ranks = cfg.ranks or (cfg.r,)
-    progress(f"rank sweep on workload {cid}: ranks {ranks}")
+    progress(f"rank sweep on {cfg.name}: ranks {ranks}")
     t = synthetic_mismatch(cfg, "A")
     h = synth.residual(cfg)
     hd = torch.from_numpy(h).cuda()
@@ -166,9 +167,9 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(cid: int, src_hash: str):
+def measured_traffic(name: str, src_hash: str):
     """HBM bytes per GEMM launch from the committed rocprofv3 counter summary, if it is current."""
-    path = os.path.join(ROOT, "profiles", f"qgemm_traffic_config{cid}.json")
+    path = os.path.join(ROOT, "profiles", f"qgemm_traffic_{name}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -207,7 +208,7 @@ def cpu_baseline(path, n_sample: int):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build measures one GPU only; --gpus must be 1",
+        print(json.dumps({"error": "this benchmark runs on one GPU only; --gpus must be 1",
                           "n_gpus": args.gpus}))
         sys.exit(2)
     import torch
@@ -216,13 +217,13 @@ def main():
         copy_probe(args.copy_probe)
         return
     if args.rank_sweep:
-        rank_sweep(args.config)
+        rank_sweep(args.workload)
         return
     from rotation_bit_post_amd.path import LayerPath
 
     t_build = time.perf_counter()
-    progress(f"building config {args.config} (sites, weights, inputs)")
-    base = LayerPath.build(args.config, keep_mismatch=not args.no_dense, prep=args.prep)
+    progress(f"building workload {args.workload} (sites, weights, inputs)")
+    base = LayerPath.build(args.workload, keep_mismatch=not args.no_dense, prep=args.prep)
     copies = [base] + [base.clone() for _ in range(args.copies - 1)]
     torch.cuda.synchronize()
     t_build = time.perf_counter() - t_build
@@ -358,7 +359,7 @@ def main():
 
     src_hash = kernel_source_hash()
     achieved = gemm_ops / (gemm_ms * 1e-3) / 1e12
-    traffic = measured_traffic(args.config, src_hash)
+    traffic = measured_traffic(cfg.name, src_hash)
     value = n / (ms_per_step * 1e-3)
     out = {
         "metric": METRIC,

@@ -41,7 +41,7 @@ import torch
 
 from . import _binding as B
 from . import offline
-from synth import CONFIGS, Config, layer_linears
+from synth import Workload, layer_linears, workload
 from synth import generators as G
 
 
@@ -93,21 +93,21 @@ def quantize_weight_on_device(w: np.ndarray, bits: int, name: str = "") -> QLine
     return QLinear(name, N, K, codes, scales)
 
 
-def synthetic_mismatch(cfg: Config, which: str) -> np.ndarray:
+def synthetic_mismatch(cfg: Workload, which: str) -> np.ndarray:
     """T (float64) of a synthetic site: rotations H C(eps A) from the seeded skew generators."""
     r_in = offline.synthetic_rotation(G.skew_generator(cfg, which, "in"), cfg.eps_rot)
     r_out = offline.synthetic_rotation(G.skew_generator(cfg, which, "out"), cfg.eps_rot)
     return offline.mismatch(r_in, r_out)
 
 
-def synthetic_site(cfg: Config, which: str, r: int):
+def synthetic_site(cfg: Workload, which: str, r: int):
     """(U_r, M) of a synthetic site."""
     return offline.convert_mismatch(synthetic_mismatch(cfg, which), r)
 
 
 @dataclass
 class LayerPath:
-    cfg: Config
+    cfg: Workload
     n: int
     r: int
     gqa: bool = True
@@ -120,12 +120,13 @@ class LayerPath:
     fp4: bool = False                              # 3-bit GEMMs on fp4 codes
 
     @classmethod
-    def build(cls, cid: int, n: int | None = None, r: int | None = None, gqa: bool = True,
+    def build(cls, wl, n: int | None = None, r: int | None = None, gqa: bool = True,
               sites=None, weights=None, keep_mismatch: bool = False, prep: str = "host",
               fp4: bool | None = None) -> "LayerPath":
         """Device-resident inputs and outputs of one layer path.
 
-        sites: optional {"A": (U, M), "B": (U, M)}; weights: optional
+        wl: the workload (a name from synth.WORKLOADS, its position there, or
+        the Workload itself). sites: optional {"A": (U, M), "B": (U, M)}; weights: optional
         {linear name: float32 (N, K)} - both default to the seeded synthetic ones.
         keep_mismatch: also keep each synthetic site's dense T (for comparisons).
         prep: "host" (float64 eigensolver on the CPU) or "device" (float64
@@ -133,7 +134,7 @@ class LayerPath:
         fp4: run the 3-bit GEMMs on fp4 codes; default: for 3-bit codes and
         more than 64 tokens (the decode-size batches keep the int8 kernels).
         """
-        cfg = CONFIGS[cid]
+        cfg = workload(wl)
         self = cls(cfg, n or cfg.n, r or cfg.r, gqa)
         self.fp4 = (cfg.bits == 3 and self.n > 64) if fp4 is None else bool(fp4)
         if self.fp4 and cfg.bits != 3:

@@ -5,7 +5,10 @@ computes none of the method: no rotation, no basis-mismatch matrix, no
 subspace, no normalisation and no quantisation. Both the CPU oracle and the
 GPU path read their inputs from here, and from nothing else they share.
 """
-from .configs import CONFIGS, Config, Linear, layer_linears
+from .workloads import (
+    WORKLOADS, Workload, Linear, layer_linears, workload,
+    TINY, LLAMA2_7B_PREFILL, LLAMA2_7B_DECODE, LLAMA3_8B_W3A3, LLAMA2_70B_PREFILL,
+)
 from .generators import (
     residual,
     skew_generator,
@@ -17,7 +20,8 @@ from .generators import (
 )
 
 __all__ = [
-    "CONFIGS", "Config", "Linear", "layer_linears",
+    "WORKLOADS", "Workload", "Linear", "layer_linears", "workload",
+    "TINY", "LLAMA2_7B_PREFILL", "LLAMA2_7B_DECODE", "LLAMA3_8B_W3A3", "LLAMA2_70B_PREFILL",
     "residual", "skew_generator", "weight", "linear_input", "outlier_channels",
     "to_bf16_bits", "bf16_bits_to_f32",
 ]

@@ -7,7 +7,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .configs import Config, INPUT_STREAMS, SKEW_STREAMS, WEIGHT_STREAMS
+from .workloads import Workload, INPUT_STREAMS, SKEW_STREAMS, WEIGHT_STREAMS
 
 
 def _rng(seed_id: int, stream: int) -> np.random.Generator:
@@ -28,12 +28,12 @@ def bf16_bits_to_f32(b) -> np.ndarray:
     return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
 
 
-def outlier_channels(cfg: Config) -> np.ndarray:
+def outlier_channels(cfg: Workload) -> np.ndarray:
     """Sorted indices of the outlier channels, drawn without replacement."""
     return np.sort(_rng(cfg.seed_id, 3).choice(cfg.D, cfg.n_outliers, replace=False))
 
 
-def residual(cfg: Config, n: int | None = None) -> np.ndarray:
+def residual(cfg: Workload, n: int | None = None) -> np.ndarray:
     """Residual stream h, shape (n, D), float32 values in the workload's storage type.
 
     Standard normal entries; the outlier channels (the same for every token)
@@ -50,7 +50,7 @@ def residual(cfg: Config, n: int | None = None) -> np.ndarray:
     return np.ascontiguousarray(h)
 
 
-def skew_generator(cfg: Config, site: str, which: str) -> np.ndarray:
+def skew_generator(cfg: Workload, site: str, which: str) -> np.ndarray:
     """Skew-symmetric D x D float64 matrix with independent N(0,1) off-diagonal entries.
 
     ``site`` is "A" (attention input) or "B" (FFN input); ``which`` is "in" or "out".
@@ -60,14 +60,14 @@ def skew_generator(cfg: Config, site: str, which: str) -> np.ndarray:
     return U - U.T
 
 
-def weight(cfg: Config, name: str, rows: int, cols: int) -> np.ndarray:
+def weight(cfg: Workload, name: str, rows: int, cols: int) -> np.ndarray:
     """Dense weight, shape (rows, cols), float32 N(0, sigma_w^2)."""
     z = _rng(cfg.seed_id, WEIGHT_STREAMS[name]).standard_normal((rows, cols), dtype=np.float32)
     z *= np.float32(cfg.sigma_w)
     return z
 
 
-def linear_input(cfg: Config, which: str, n: int, width: int) -> np.ndarray:
+def linear_input(cfg: Workload, which: str, n: int, width: int) -> np.ndarray:
     """Stand-in input of a linear not fed by a correction site (o_proj or down_proj).
 
     N(0,1), no outliers, rounded to bf16 for bf16 workloads.

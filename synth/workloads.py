@@ -2,8 +2,8 @@
 
 Shapes borrow the LLaMA models the ReSpinQuant pages evaluate (technical
 summary, "Results" section: LLaMA-2 7B/13B, LLaMA-3 8B, LLaMA-3.2 1B/3B); the
-outlier channels stand in for the "extreme outliers in activation channels"
-named in each page's "Problem" section. No dataset or trained weight is used.
+outlier channels stand in for the large activation outliers described in
+each page's "Problem" section. No dataset or trained weight is used.
 
 Seed streams (``numpy.random.SeedSequence([seed_id, stream])``):
   0 residual h, 3 outlier channel indices,
@@ -18,9 +18,8 @@ from typing import Optional, Tuple
 
 
 @dataclass(frozen=True)
-class Config:
-    cid: int                 # workload number, 1..5
-    name: str
+class Workload:
+    name: str                # model, phase and bit widths
     seed_id: int             # seed family (the decode workload reuses the prefill one)
     D: int                   # hidden size (residual width)
     F: Optional[int]         # FFN width (None: single-linear block)
@@ -39,23 +38,45 @@ class Config:
     single_linear: Optional[Tuple[int, int]] = None  # (N, K) of the one linear of a tiny block
 
 
-CONFIGS = {
-    1: Config(1, "tiny-d256-r8", 1, D=256, F=None, r=8, n=16, bits=4, h_dtype="f32",
-              y_dtype="f32", eps_rot=0.02, n_outliers=4, outlier_scale=40.0, sigma_w=0.02,
-              single_linear=(256, 256)),
-    2: Config(2, "llama2-7b-prefill-w4a4", 2, D=4096, F=11008, r=32, n=2048, bits=4,
-              h_dtype="bf16", y_dtype="bf16", eps_rot=0.01, n_outliers=20,  # 0.5% of 4096
-              outlier_scale=50.0, sigma_w=0.02, kv=None),
-    3: Config(3, "llama2-7b-decode-w4a4", 2, D=4096, F=11008, r=32, n=64, bits=4,
-              h_dtype="bf16", y_dtype="bf16", eps_rot=0.01, n_outliers=20,
-              outlier_scale=50.0, sigma_w=0.02, kv=None, decode_batches=(1, 8, 64)),
-    4: Config(4, "llama3-8b-prefill-w3a3", 4, D=4096, F=14336, r=32, n=4096, bits=3,
-              h_dtype="bf16", y_dtype="bf16", eps_rot=0.01, n_outliers=41,  # 1% of 4096
-              outlier_scale=30.0, sigma_w=0.02, kv=1024, ranks=(8, 16, 32, 64)),
-    5: Config(5, "llama2-70b-prefill-w4a4", 5, D=8192, F=28672, r=32, n=4096, bits=4,
-              h_dtype="bf16", y_dtype="bf16", eps_rot=0.01, n_outliers=25,  # 0.3% of 8192
-              outlier_scale=60.0, sigma_w=0.01, kv=1024),
-}
+TINY = "tiny-d256-r8"                       # one 256 x 256 linear, 16 tokens
+LLAMA2_7B_PREFILL = "llama2-7b-prefill-w4a4"  # D 4096, FFN 11008, 2048 tokens
+LLAMA2_7B_DECODE = "llama2-7b-decode-w4a4"    # D 4096, FFN 11008, 1 to 64 tokens
+LLAMA3_8B_W3A3 = "llama3-8b-prefill-w3a3"     # D 4096, FFN 14336, k/v 1024, 4096 tokens
+LLAMA2_70B_PREFILL = "llama2-70b-prefill-w4a4"  # D 8192, FFN 28672, k/v 1024, 4096 tokens
+
+WORKLOADS = {w.name: w for w in (
+    Workload(TINY, 1, D=256, F=None, r=8, n=16, bits=4, h_dtype="f32",
+             y_dtype="f32", eps_rot=0.02, n_outliers=4, outlier_scale=40.0, sigma_w=0.02,
+             single_linear=(256, 256)),
+    Workload(LLAMA2_7B_PREFILL, 2, D=4096, F=11008, r=32, n=2048, bits=4,
+             h_dtype="bf16", y_dtype="bf16", eps_rot=0.01, n_outliers=20,  # 0.5% of 4096
+             outlier_scale=50.0, sigma_w=0.02, kv=None),
+    Workload(LLAMA2_7B_DECODE, 2, D=4096, F=11008, r=32, n=64, bits=4,
+             h_dtype="bf16", y_dtype="bf16", eps_rot=0.01, n_outliers=20,
+             outlier_scale=50.0, sigma_w=0.02, kv=None, decode_batches=(1, 8, 64)),
+    Workload(LLAMA3_8B_W3A3, 4, D=4096, F=14336, r=32, n=4096, bits=3,
+             h_dtype="bf16", y_dtype="bf16", eps_rot=0.01, n_outliers=41,  # 1% of 4096
+             outlier_scale=30.0, sigma_w=0.02, kv=1024, ranks=(8, 16, 32, 64)),
+    Workload(LLAMA2_70B_PREFILL, 5, D=8192, F=28672, r=32, n=4096, bits=4,
+             h_dtype="bf16", y_dtype="bf16", eps_rot=0.01, n_outliers=25,  # 0.3% of 8192
+             outlier_scale=60.0, sigma_w=0.01, kv=1024),
+)}
+
+
+def workload(key) -> Workload:
+    """A workload by name, or by its 1-based position in WORKLOADS."""
+    if isinstance(key, Workload):
+        return key
+    if isinstance(key, int) or (isinstance(key, str) and key.isdigit()):
+        names = list(WORKLOADS)
+        i = int(key)
+        if not 1 <= i <= len(names):
+            raise KeyError(f"no workload at position {i}; positions 1..{len(names)}")
+        return WORKLOADS[names[i - 1]]
+    if key not in WORKLOADS:
+        raise KeyError(f"unknown workload {key!r}; known: {', '.join(WORKLOADS)}")
+    return WORKLOADS[key]
+
 
 # weight name -> seed stream
 WEIGHT_STREAMS = {"q": 4, "k": 5, "v": 6, "o": 7, "gate": 8, "up": 9, "down": 10, "proj": 4}
@@ -72,7 +93,7 @@ class Linear:
     parts: Tuple[Tuple[str, int], ...] = field(default=())  # stacked weights (name, rows)
 
 
-def layer_linears(cfg: Config, gqa: bool = True):
+def layer_linears(cfg: Workload, gqa: bool = True):
     """The linears of one decoder layer in execution order.
 
     Site A (attention input) feeds the fused q|k|v projection, the o_proj

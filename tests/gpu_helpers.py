@@ -46,25 +46,25 @@ def empty_f32(*shape):
 
 
 @functools.lru_cache(maxsize=None)
-def oracle_site(cid: int, which: str, r: int):
+def oracle_site(wl, which: str, r: int):
     """Oracle prep of a synthetic site (float64 SVD), cached per test session."""
-    cfg = synth.CONFIGS[cid]
+    cfg = synth.workload(wl)
     s = prep.site(synth.skew_generator(cfg, which, "in"), synth.skew_generator(cfg, which, "out"), cfg.eps_rot, r)
     return s["U32"], s["M32"], s["sigma"]
 
 
 @functools.lru_cache(maxsize=None)
-def oracle_basis_all(cid: int, which: str, r_max: int):
+def oracle_basis_all(wl, which: str, r_max: int):
     """U (all ranks up to r_max) and T of a site: one SVD serves a rank sweep."""
-    cfg = synth.CONFIGS[cid]
+    cfg = synth.workload(wl)
     t = prep.basis_mismatch(prep.rotation(synth.skew_generator(cfg, which, "in"), cfg.eps_rot),
                             prep.rotation(synth.skew_generator(cfg, which, "out"), cfg.eps_rot))
     u, sigma = prep.principal_subspace(t, r_max)
     return u, t, sigma
 
 
-def site_for_rank(cid: int, which: str, r: int, r_max: int = 64):
-    u, t, _ = oracle_basis_all(cid, which, r_max)
+def site_for_rank(wl, which: str, r: int, r_max: int = 64):
+    u, t, _ = oracle_basis_all(wl, which, r_max)
     ur = u[:, :r]
     m = prep.subspace_transform(t, ur)
     return ur.astype(np.float32), m.astype(np.float32)

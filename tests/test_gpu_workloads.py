@@ -105,12 +105,12 @@ def gemm_sampled(bits, n, N, K, seed, rows=None, cols=None, y_dtype="bf16", fp4=
           flush=True)
 
 
-# ------------------------------------------------------------------ config 1
-def test_config1_tiny_block_end_to_end():
+# ------------------------------------------------------- tiny block, d = 256
+def test_tiny_block_end_to_end():
     import torch
     rsq = lib()
-    cfg = synth.CONFIGS[1]
-    U, M, _ = oracle_site(1, "A", cfg.r)
+    cfg = synth.WORKLOADS[synth.TINY]
+    U, M, _ = oracle_site(synth.TINY, "A", cfg.r)
     h = synth.residual(cfg)
     w = synth.weight(cfg, "proj", *cfg.single_linear)
     qw, sw = prep.quantize_weight(w, cfg.bits)
@@ -135,30 +135,30 @@ def test_config1_tiny_block_end_to_end():
     assert np.all(np.abs(wsc.cpu().numpy() - sw) <= 1e-6 * sw)
 
 
-# ------------------------------------------------------------- configs 2, 3
-def test_config2_both_sites_full_batch():
-    cfg = synth.CONFIGS[2]
+# --------------------------------- llama2-7b, prefill (2048 tokens) and decode
+def test_llama2_7b_prefill_both_sites_full_batch():
+    cfg = synth.WORKLOADS[synth.LLAMA2_7B_PREFILL]
     h = synth.residual(cfg)
-    print(f"case config2 sites n={cfg.n} d={cfg.D} r={cfg.r}", flush=True)
-    UA, MA, _ = oracle_site(2, "A", cfg.r)
+    print(f"case llama2-7b prefill sites n={cfg.n} d={cfg.D} r={cfg.r}", flush=True)
+    UA, MA, _ = oracle_site(synth.LLAMA2_7B_PREFILL, "A", cfg.r)
     outA, cA, sA = run_site(to_dev(h, "bf16"), UA, MA, cfg.bits, "bf16")
     hA, _, _ = check_site(h, UA, MA, "bf16", cfg.bits, outA, cA, sA)
-    UB, MB, _ = oracle_site(2, "B", cfg.r)
+    UB, MB, _ = oracle_site(synth.LLAMA2_7B_PREFILL, "B", cfg.r)
     outB, cB, sB = run_site(outA, UB, MB, cfg.bits, "bf16")
     check_site(hA, UB, MB, "bf16", cfg.bits, outB, cB, sB)
 
 
 @pytest.mark.parametrize("name,N,K", [("qkv", 12288, 4096), ("o", 4096, 4096), ("gate_up", 22016, 4096),
                                       ("down", 4096, 11008)])
-def test_config2_gemms_full_size(name, N, K):
-    print(f"case config2 gemm {name}", flush=True)
+def test_llama2_7b_prefill_gemms_full_size(name, N, K):
+    print(f"case llama2-7b prefill gemm {name}", flush=True)
     gemm_sampled(4, 2048, N, K, seed=N + K)
 
 
-def test_config2_weight_quantisation_on_device():
+def test_llama2_7b_weight_quantisation_on_device():
     import torch
     rsq = lib()
-    cfg = synth.CONFIGS[2]
+    cfg = synth.WORKLOADS[synth.LLAMA2_7B_PREFILL]
     w = np.concatenate([synth.weight(cfg, p, cfg.D, cfg.D) for p in ("q", "k", "v")], axis=0)
     wc, wsc = empty_u8(w.shape[0], cfg.D // 2), empty_f32(w.shape[0])
     rsq.rsq_quant_act(to_dev(w, "f32"), wc, wsc, cfg.bits)
@@ -170,14 +170,14 @@ def test_config2_weight_quantisation_on_device():
 
 
 @pytest.mark.parametrize("n", [1, 8, 64])
-def test_config3_decode_batches(n):
+def test_llama2_7b_decode_batches(n):
     import torch
     rsq = lib()
-    cfg = synth.CONFIGS[3]
-    print(f"case config3 decode n={n}", flush=True)
+    cfg = synth.WORKLOADS[synth.LLAMA2_7B_DECODE]
+    print(f"case llama2-7b decode decode n={n}", flush=True)
     h = synth.residual(cfg, n)
-    assert np.array_equal(h, synth.residual(synth.CONFIGS[2], 2048)[:n])   # head of the prefill batch
-    UA, MA, _ = oracle_site(2, "A", cfg.r)
+    assert np.array_equal(h, synth.residual(synth.WORKLOADS[synth.LLAMA2_7B_PREFILL], 2048)[:n])   # head of the prefill batch
+    UA, MA, _ = oracle_site(synth.LLAMA2_7B_PREFILL, "A", cfg.r)
     out, codes, scales = run_site(to_dev(h, "bf16"), UA, MA, cfg.bits, "bf16")
     _, q_gpu, s_gpu = check_site(h, UA, MA, "bf16", cfg.bits, out, codes, scales)
     # q|k|v projection with the real quantised weights, every output checked
@@ -193,17 +193,17 @@ def test_config3_decode_batches(n):
         gemm_sampled(4, n, N, K, seed=n + N, rows=np.arange(n))
 
 
-# ------------------------------------------------------------------ config 4
-def test_config4_w3a3_rank_sweep():
-    cfg = synth.CONFIGS[4]
+# ------------------------------------------------ llama3-8b w3a3, 4096 tokens
+def test_llama3_8b_w3a3_rank_sweep():
+    cfg = synth.WORKLOADS[synth.LLAMA3_8B_W3A3]
     h = synth.residual(cfg)
     hd = to_dev(h, "bf16")
-    _, T, _ = oracle_basis_all(4, "A", 64)
+    _, T, _ = oracle_basis_all(synth.LLAMA3_8B_W3A3, "A", 64)
     dense = np.asarray(h, np.float64) @ T
     errs = []
     for r in cfg.ranks:
-        print(f"case config4 site r={r}", flush=True)
-        U, M = site_for_rank(4, "A", r)
+        print(f"case llama3-8b w3a3 site r={r}", flush=True)
+        U, M = site_for_rank(synth.LLAMA3_8B_W3A3, "A", r)
         out, codes, scales = run_site(hd, U, M, 3, "bf16")
         hp, _, _ = check_site(h, U, M, "bf16", 3, out, codes, scales)
         errs.append(rel_l2(hp, dense))
@@ -218,10 +218,10 @@ def test_dense_comparator_against_oracle():
     from it equals the oracle's approximation error."""
     import torch
     rsq = lib()
-    cfg = synth.CONFIGS[4]
+    cfg = synth.WORKLOADS[synth.LLAMA3_8B_W3A3]
     h = synth.residual(cfg, 512)
     hd = to_dev(h, "bf16")
-    _, T, _ = oracle_basis_all(4, "A", 64)
+    _, T, _ = oracle_basis_all(synth.LLAMA3_8B_W3A3, "A", 64)
     dense_gpu = to_host(torch.matmul(hd, torch.from_numpy(T.astype(np.float32)).cuda().to(torch.bfloat16)))
     rows = np.arange(0, 512, 7)
     ref = np.asarray(h, np.float64)[rows] @ T
@@ -229,7 +229,7 @@ def test_dense_comparator_against_oracle():
     print(f"  dense bf16 h T rel_l2 vs float64 oracle: {err_dense:.2e}", flush=True)
     assert err_dense < 2e-2
     r = cfg.r
-    U, M = site_for_rank(4, "A", r)
+    U, M = site_for_rank(synth.LLAMA3_8B_W3A3, "A", r)
     out = torch.empty_like(hd)
     rsq.rsq_subspace_correct(hd, out, gpu_site(U, M), r)
     torch.cuda.synchronize()
@@ -241,12 +241,12 @@ def test_dense_comparator_against_oracle():
 
 @pytest.mark.parametrize("fp4", [False, True])
 @pytest.mark.parametrize("name,N,K", [("qkv_gqa", 6144, 4096), ("gate_up", 28672, 4096), ("down", 4096, 14336)])
-def test_config4_w3a3_gemms_full_size(name, N, K, fp4):
-    print(f"case config4 gemm {name} fp4={fp4}", flush=True)
+def test_llama3_8b_w3a3_gemms_full_size(name, N, K, fp4):
+    print(f"case llama3-8b w3a3 gemm {name} fp4={fp4}", flush=True)
     gemm_sampled(3, 4096, N, K, seed=N + K + 4, fp4=fp4)
 
 
-def test_config4_layer_on_fp4_codes_equals_the_int3_layer():
+def test_llama3_8b_w3a3_layer_on_fp4_codes_equals_the_int3_layer():
     """The W3A3 layer (chained, 320 tokens) with its codes written as fp4 and its
     GEMMs on the fp4 matrix cores writes the same bits as with int3 codes and
     the int3 GEMMs (themselves checked against the oracle): every residual,
@@ -255,14 +255,14 @@ def test_config4_layer_on_fp4_codes_equals_the_int3_layer():
     import torch
     from rotation_bit_post_amd import RSQ_FP4
     from rotation_bit_post_amd.path import LayerPath
-    cfg = synth.CONFIGS[4]
-    print("case config4 layer fp4 vs int3", flush=True)
+    cfg = synth.WORKLOADS[synth.LLAMA3_8B_W3A3]
+    print("case llama3-8b w3a3 layer fp4 vs int3", flush=True)
     # any valid sites serve here (both paths get the same ones; the int3 layer
     # is checked against the oracle elsewhere): seeded subspace sites, no SVD
     sites = {"A": subspace_site(cfg.D, cfg.r, seed=41), "B": subspace_site(cfg.D, cfg.r, seed=42)}
-    p4 = LayerPath.build(4, n=320, sites=sites)
+    p4 = LayerPath.build(synth.LLAMA3_8B_W3A3, n=320, sites=sites)
     print("  fp4 layer built", flush=True)
-    p3 = LayerPath.build(4, n=320, sites=sites, fp4=False)
+    p3 = LayerPath.build(synth.LLAMA3_8B_W3A3, n=320, sites=sites, fp4=False)
     assert p4.fp4 and p4.code_bits == 3 | RSQ_FP4 and not p3.fp4
     assert [nm for nm, _, _ in p4.stages(chain=True)] == [nm for nm, _, _ in p3.stages(chain=True)]
     for chain in (False, True):
@@ -283,35 +283,35 @@ def test_config4_layer_on_fp4_codes_equals_the_int3_layer():
         assert np.array_equal(lin.fp4.cpu().numpy(), packing.pack_fp4(q)), name
 
 
-# ------------------------------------------------------------------ config 5
+# ----------------------------------------------- llama2-70b prefill, d = 8192
 @pytest.mark.timeout(600)
-def test_config5_site_full_batch():
-    cfg = synth.CONFIGS[5]
-    print("case config5 site (float64 SVD of an 8192 x 8192 matrix first)", flush=True)
-    U, M, _ = oracle_site(5, "A", cfg.r)
+def test_llama2_70b_site_full_batch():
+    cfg = synth.WORKLOADS[synth.LLAMA2_70B_PREFILL]
+    print("case llama2-70b site (float64 SVD of an 8192 x 8192 matrix first)", flush=True)
+    U, M, _ = oracle_site(synth.LLAMA2_70B_PREFILL, "A", cfg.r)
     h = synth.residual(cfg)
     out, codes, scales = run_site(to_dev(h, "bf16"), U, M, cfg.bits, "bf16")
     check_site(h, U, M, "bf16", cfg.bits, out, codes, scales)
 
 
 @pytest.mark.parametrize("name,N,K", [("qkv_gqa", 10240, 8192), ("gate_up", 57344, 8192), ("down", 8192, 28672)])
-def test_config5_gemms_full_size(name, N, K):
-    print(f"case config5 gemm {name}", flush=True)
+def test_llama2_70b_gemms_full_size(name, N, K):
+    print(f"case llama2-70b gemm {name}", flush=True)
     gemm_sampled(4, 4096, N, K, seed=N + K + 5)
 
 
-# ------------------------------------------------------- chained layer (config 2)
-def test_config2_layer_chained_stage_by_stage():
+# ---------------------------------------- chained layer (llama2-7b prefill)
+def test_llama2_7b_prefill_layer_chained_stage_by_stage():
     """A decoder layer with the residual stream carried through (sites A and B,
     o_proj and down_proj added to the residual in the GEMM epilogue): every
     stage checked on sampled tokens against the oracle fed the GPU's own inputs."""
     import torch
     from rotation_bit_post_amd.path import LayerPath
-    cfg = synth.CONFIGS[2]
+    cfg = synth.WORKLOADS[synth.LLAMA2_7B_PREFILL]
     n = 256
-    ua, ma, _ = oracle_site(2, "A", cfg.r)
-    ub, mb, _ = oracle_site(2, "B", cfg.r)
-    path = LayerPath.build(2, n=n, sites={"A": (ua, ma), "B": (ub, mb)})
+    ua, ma, _ = oracle_site(synth.LLAMA2_7B_PREFILL, "A", cfg.r)
+    ub, mb, _ = oracle_site(synth.LLAMA2_7B_PREFILL, "B", cfg.r)
+    path = LayerPath.build(synth.LLAMA2_7B_PREFILL, n=n, sites={"A": (ua, ma), "B": (ub, mb)})
     for _, _, fn in path.stages(correction=True, chain=True):
         fn()
     torch.cuda.synchronize()
@@ -354,10 +354,10 @@ def test_layer_step_replayed_as_a_hip_graph_matches_eager():
     import torch
     from rotation_bit_post_amd.path import LayerPath
     rsq = lib()
-    cfg = synth.CONFIGS[2]
-    ua, ma, _ = oracle_site(2, "A", cfg.r)
-    ub, mb, _ = oracle_site(2, "B", cfg.r)
-    path = LayerPath.build(2, n=192, sites={"A": (ua, ma), "B": (ub, mb)})
+    cfg = synth.WORKLOADS[synth.LLAMA2_7B_PREFILL]
+    ua, ma, _ = oracle_site(synth.LLAMA2_7B_PREFILL, "A", cfg.r)
+    ub, mb, _ = oracle_site(synth.LLAMA2_7B_PREFILL, "B", cfg.r)
+    path = LayerPath.build(synth.LLAMA2_7B_PREFILL, n=192, sites={"A": (ua, ma), "B": (ub, mb)})
     path.step(chain=True)
     torch.cuda.synchronize()
     ref = {k: v.clone() for k, v in path.outputs(chain=True).items()}
@@ -382,10 +382,10 @@ def test_fp4_layer_step_replayed_as_a_hip_graph_matches_eager():
     import torch
     from rotation_bit_post_amd.path import LayerPath
     rsq = lib()
-    cfg = synth.CONFIGS[4]
-    print("case config4 fp4 layer graph replay", flush=True)
+    cfg = synth.WORKLOADS[synth.LLAMA3_8B_W3A3]
+    print("case llama3-8b w3a3 fp4 layer graph replay", flush=True)
     sites = {"A": subspace_site(cfg.D, cfg.r, seed=43), "B": subspace_site(cfg.D, cfg.r, seed=44)}
-    path = LayerPath.build(4, n=192, sites=sites, fp4=True)
+    path = LayerPath.build(synth.LLAMA3_8B_W3A3, n=192, sites=sites, fp4=True)
     path.step(chain=True)
     torch.cuda.synchronize()
     ref = {k: v.clone() for k, v in path.outputs(chain=True).items()}
@@ -408,14 +408,14 @@ def test_device_offline_prep_matches_oracle_at_full_size():
     subspace iteration) spans the oracle's SVD subspace and acts as the same operator."""
     import torch
     from rotation_bit_post_amd import offline_device as OD
-    cfg = synth.CONFIGS[2]
-    print("case device prep config 2 site A", flush=True)
+    cfg = synth.WORKLOADS[synth.LLAMA2_7B_PREFILL]
+    print("case device prep llama2-7b prefill site A", flush=True)
     r_in = OD.synthetic_rotation_device(synth.skew_generator(cfg, "A", "in"), cfg.eps_rot)
     r_out = OD.synthetic_rotation_device(synth.skew_generator(cfg, "A", "out"), cfg.eps_rot)
     u, m, iters, res = OD.convert_site_device(r_in, r_out, cfg.r)
     print(f"  {iters} iterations, residual {res:.2e}", flush=True)
     assert res < 1e-9
-    uo, mo, _ = oracle_site(2, "A", cfg.r)
+    uo, mo, _ = oracle_site(synth.LLAMA2_7B_PREFILL, "A", cfg.r)
     x = np.random.default_rng(5).standard_normal((16, cfg.D))
     act = lambda uu, mm: x + ((x @ uu.astype(np.float64)) @ mm.astype(np.float64)) @ uu.astype(np.float64).T  # noqa: E731
     assert rel_l2(act(u, m), act(uo, mo)) < 1e-5

@@ -31,8 +31,8 @@ def test_site_operator_matches_oracle(d, r, eps):
     assert np.allclose(U.T.astype(np.float64) @ U, np.eye(r), atol=1e-6)
 
 
-def test_config1_site_matches_oracle():
-    cfg = synth.CONFIGS[1]
+def test_tiny_site_matches_oracle():
+    cfg = synth.WORKLOADS[synth.TINY]
     a_in, a_out = synth.skew_generator(cfg, "A", "in"), synth.skew_generator(cfg, "A", "out")
     U, M = offline.convert_site(offline.synthetic_rotation(a_in, cfg.eps_rot),
                                 offline.synthetic_rotation(a_out, cfg.eps_rot), cfg.r)

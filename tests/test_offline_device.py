@@ -17,7 +17,7 @@ def _operator(u, m):
 
 @pytest.mark.parametrize("r", [8, 16])
 def test_device_conversion_matches_oracle_subspace_and_operator(r):
-    cfg = synth.CONFIGS[1]
+    cfg = synth.WORKLOADS[synth.TINY]
     a_in, a_out = synth.skew_generator(cfg, "A", "in"), synth.skew_generator(cfg, "A", "out")
     s = prep.site(a_in, a_out, cfg.eps_rot, r)
     r_in = synthetic_rotation_device(a_in, cfg.eps_rot, device="cpu")
@@ -33,14 +33,14 @@ def test_device_conversion_matches_oracle_subspace_and_operator(r):
 
 
 def test_device_rotation_equals_host_rotation():
-    cfg = synth.CONFIGS[1]
+    cfg = synth.WORKLOADS[synth.TINY]
     a = synth.skew_generator(cfg, "B", "in")
     r_dev = synthetic_rotation_device(a, cfg.eps_rot, device="cpu").numpy()
     assert np.max(np.abs(r_dev - prep.rotation(a, cfg.eps_rot))) < 1e-12
 
 
 def test_device_conversion_refuses_a_rank_inside_a_pair():
-    cfg = synth.CONFIGS[1]
+    cfg = synth.WORKLOADS[synth.TINY]
     a_in, a_out = synth.skew_generator(cfg, "A", "in"), synth.skew_generator(cfg, "A", "out")
     r_in = synthetic_rotation_device(a_in, cfg.eps_rot, device="cpu")
     r_out = synthetic_rotation_device(a_out, cfg.eps_rot, device="cpu")
