@@ -51,7 +51,10 @@ def parse():
     p.add_argument("--prep", choices=("device", "host"), default="device",
                    help="where the synthetic sites are prepared (offline step, not timed in the step)")
     p.add_argument("--rank-sweep", action="store_true",
-                   help="only the correction at every rank of the workload (time and error against dense h T)")
+                   help="only the correction at every rank of the workload: its time, its error against dense h T "
+                        "and the end-to-end error of the site's linear")
+    p.add_argument("--mismatch", choices=("dense", "lowrank"), default="dense",
+                   help="the rank sweep's site mismatch: the workload's (dense) or one with T - I of rank <= 64")
     p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                    help="only run a plain device copy of MIB MiB (calibrates rocprofv3 byte counters) and exit")
     return p.parse_args()
@@ -122,39 +125,90 @@ def dense_comparator(path, which: str = "A", iters: int = 20):
     }
 
 
-def rank_sweep(wl, iters: int = 20):
-    """Correction time and distance from dense h T at every rank of the workload."""
+def rank_sweep(wl, mismatch: str = "dense", iters: int = 20):
+    """Per rank of the workload: the correction's time, its distance from the dense h T, and the
+    end-to-end error of the site's linear (q|k|v) against an unquantised float64 layer with dense T.
+
+    mismatch: "dense" - the workload's site A (Cayley rotations of dense skew generators, T - I
+    of full rank); "lowrank" - rotations whose skew generators have rank 2k = 32 (step 1), so T - I
+    has rank at most 64 and the rank-64 correction is exact.
+    Rank 0 is the path without a correction (RMSNorm + quantisation of h itself). The float64
+    references are plain torch arithmetic on the GPU: they measure the method's error, they are
+    not the parity oracle.
+    """
     import torch
     import rotation_bit_post_amd as B
     from rotation_bit_post_amd import offline
-    from rotation_bit_post_amd.path import make_site, synthetic_mismatch
+    from rotation_bit_post_amd.path import make_site, synthetic_mismatch, quantize_weight_on_device
     import synth
     cfg = synth.workload(wl)
+    eps = 1e-5
     ranks = cfg.ranks or (cfg.r,)
-    progress(f"rank sweep on {cfg.name}: ranks {ranks}")
-    t = synthetic_mismatch(cfg, "A")
+    progress(f"rank sweep on {cfg.name} ({mismatch} mismatch): ranks {ranks}")
+    if mismatch == "lowrank":
+        k, step = 16, 1.0
+        t = offline.mismatch(offline.synthetic_rotation(synth.low_rank_skew(cfg, "A", "in", k), step),
+                             offline.synthetic_rotation(synth.low_rank_skew(cfg, "A", "out", k), step))
+    else:
+        t = synthetic_mismatch(cfg, "A")
     h = synth.residual(cfg)
     hd = torch.from_numpy(h).cuda()
     hd = hd.to(torch.bfloat16) if cfg.h_dtype == "bf16" else hd
     ref = hd.float() @ torch.from_numpy(t.astype(np.float32)).cuda()
+    nrm = torch.linalg.vector_norm
+
+    # the site's linear, unquantised, in float64 with the dense T
+    lin = next(l for l in synth.layer_linears(cfg) if l.source == "siteA")
+    w = np.concatenate([synth.weight(cfg, part, rows, lin.K) for part, rows in lin.parts], axis=0)
+    w64 = torch.from_numpy(w).cuda().double()
+    h64 = hd.double()
+
+    def layer64(x):  # RMSNorm (unit weight) and the linear, float64
+        return (x * torch.rsqrt((x * x).mean(dim=1, keepdim=True) + eps)) @ w64.T
+
+    y_ref = layer64(h64 @ torch.from_numpy(t).cuda())
+    wq = quantize_weight_on_device(w, cfg.bits, lin.name)
+    y = torch.empty((cfg.n, lin.N), dtype=torch.bfloat16 if cfg.y_dtype == "bf16" else torch.float32, device="cuda")
+    codes = torch.empty((cfg.n, B.rsq_packed_row_bytes(cfg.D, cfg.bits)), dtype=torch.uint8, device="cuda")
+    scales = torch.empty(cfg.n, dtype=torch.float32, device="cuda")
+
+    def y_error():
+        B.rsq_qgemm(codes, scales, cfg.n, wq.codes, wq.scales, lin.N, lin.K, cfg.bits, y)
+        return float(nrm(y.double() - y_ref) / nrm(y_ref))
+
     stream = torch.cuda.current_stream()
-    rows = []
+    B.rsq_quant_act(hd, codes, scales, cfg.bits, rmsnorm=True, eps=eps)
+    rows = [{"r": 0, "rel_l2_vs_dense_hT": round(float(nrm(hd.float() - ref) / nrm(ref)), 5),
+             "y_rel_l2_unquantised": round(float(nrm(layer64(h64) - y_ref) / nrm(y_ref)), 5),
+             "y_rel_l2_quantised": round(y_error(), 5)}]
+    progress(f"r=0: y error {rows[0]['y_rel_l2_quantised']:.4f}")
     for r in ranks:
         U, M = offline.convert_mismatch(t, r)
         site = make_site(U, M)
         out = torch.empty_like(hd)
-        codes = torch.empty((cfg.n, B.rsq_packed_row_bytes(cfg.D, cfg.bits)), dtype=torch.uint8, device="cuda")
-        scales = torch.empty(cfg.n, dtype=torch.float32, device="cuda")
         ms_c = _time_ms(lambda: B.rsq_subspace_correct(hd, out, site.buf, r), iters, stream)
         ms_q = _time_ms(lambda: B.rsq_correct_quant(hd, out, site.buf, r, codes, scales, cfg.bits), iters, stream)
         B.rsq_subspace_correct(hd, out, site.buf, r)
-        err = float(torch.linalg.vector_norm(out.float() - ref) / torch.linalg.vector_norm(ref))
+        err = float(nrm(out.float() - ref) / nrm(ref))
+        u64, m64 = torch.from_numpy(U).cuda().double(), torch.from_numpy(M).cuda().double()
+        y_apx = layer64(h64 + ((h64 @ u64) @ m64) @ u64.T)
+        B.rsq_correct_quant(hd, out, site.buf, r, codes, scales, cfg.bits, eps=eps)
         rows.append({"r": r, "correction_ms": round(ms_c, 5), "correction_norm_quant_ms": round(ms_q, 5),
-                     "rel_l2_vs_dense_hT": round(err, 5)})
-        progress(f"r={r}: {ms_c * 1e3:.1f} us, error {err:.4f}")
-    print(json.dumps({"rank_sweep": rows, "workload": f"{cfg.name}: D={cfg.D}, {cfg.n} tokens, {cfg.h_dtype}",
-                      "note": "error of the rank-r correction against the dense product h T (float32); "
-                              "the synthetic rotations are far from I, so the error falls slowly with r"}),
+                     "rel_l2_vs_dense_hT": round(err, 5),
+                     "y_rel_l2_unquantised": round(float(nrm(y_apx - y_ref) / nrm(y_ref)), 5),
+                     "y_rel_l2_quantised": round(y_error(), 5)})
+        progress(f"r={r}: {ms_c * 1e3:.1f} us, correction error {err:.4f}, y error {rows[-1]['y_rel_l2_quantised']:.4f}")
+    print(json.dumps({"rank_sweep": rows, "mismatch": mismatch,
+                      "workload": f"{cfg.name}: D={cfg.D}, {cfg.n} tokens, {cfg.h_dtype}, "
+                                  f"W{cfg.bits}A{cfg.bits}, linear {lin.name} {lin.N}x{lin.K}",
+                      "note": "rel_l2_vs_dense_hT: the corrected residual (GPU) against the dense product h T "
+                              "(float32); y_rel_l2_unquantised: the site's linear on the rank-r approximation, "
+                              "unquantised float64, against the same with dense T (the approximation alone); "
+                              "y_rel_l2_quantised: the GPU path (correction, RMSNorm, per-token quantisation, "
+                              "low-bit GEMM with per-channel weight codes) against that float64 reference; "
+                              "r = 0: no correction. dense: the synthetic rotations are far from I and "
+                              "T - I has full rank, so the approximation error falls slowly with r; "
+                              "lowrank: T - I has rank at most 64"}),
           flush=True)
 
 
@@ -224,7 +278,7 @@ def main():
         copy_probe(args.copy_probe)
         return
     if args.rank_sweep:
-        rank_sweep(args.workload)
+        rank_sweep(args.workload, args.mismatch)
         return
     from rotation_bit_post_amd.path import LayerPath
 

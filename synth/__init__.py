@@ -12,6 +12,7 @@ from .workloads import (
 from .generators import (
     residual,
     skew_generator,
+    low_rank_skew,
     weight,
     linear_input,
     outlier_channels,
@@ -22,6 +23,6 @@ from .generators import (
 __all__ = [
     "WORKLOADS", "Workload", "Linear", "layer_linears", "workload",
     "TINY", "LLAMA2_7B_PREFILL", "LLAMA2_7B_DECODE", "LLAMA3_8B_W3A3", "LLAMA2_70B_PREFILL",
-    "residual", "skew_generator", "weight", "linear_input", "outlier_channels",
+    "residual", "skew_generator", "low_rank_skew", "weight", "linear_input", "outlier_channels",
     "to_bf16_bits", "bf16_bits_to_f32",
 ]

@@ -7,7 +7,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .workloads import Workload, INPUT_STREAMS, SKEW_STREAMS, WEIGHT_STREAMS
+from .workloads import Workload, INPUT_STREAMS, LOW_RANK_STREAMS, SKEW_STREAMS, WEIGHT_STREAMS
 
 
 def _rng(seed_id: int, stream: int) -> np.random.Generator:
@@ -58,6 +58,22 @@ def skew_generator(cfg: Workload, site: str, which: str) -> np.ndarray:
     G = _rng(cfg.seed_id, SKEW_STREAMS[(site, which)]).standard_normal((cfg.D, cfg.D))
     U = np.triu(G, 1)
     return U - U.T
+
+
+def low_rank_skew(cfg: Workload, site: str, which: str, k: int) -> np.ndarray:
+    """Skew-symmetric D x D float64 matrix of rank 2k: (P Q^T - Q P^T) / D, P and Q independent
+    D x k standard normal draws (spectral norm about 1).
+
+    A rotation built from it differs from its start only inside a 2k-dimensional subspace, so
+    the mismatch between two such rotations has rank at most 4k.
+    """
+    if not 1 <= 2 * k <= cfg.D:
+        raise ValueError("k out of range")
+    rng = _rng(cfg.seed_id, LOW_RANK_STREAMS[(site, which)])
+    P = rng.standard_normal((cfg.D, k))
+    Q = rng.standard_normal((cfg.D, k))
+    S = P @ Q.T
+    return (S - S.T) / cfg.D
 
 
 def weight(cfg: Workload, name: str, rows: int, cols: int) -> np.ndarray:

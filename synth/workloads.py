@@ -9,7 +9,9 @@ Seed streams (``numpy.random.SeedSequence([seed_id, stream])``):
   0 residual h, 3 outlier channel indices,
   1/2 site-A skew generators (in/out), 13/14 site-B skew generators (in/out),
   4..10 weights q, k, v, o, gate, up, down,
-  11 o_proj input stand-in, 12 down_proj input stand-in.
+  11 o_proj input stand-in, 12 down_proj input stand-in,
+  15/16 site-A and 17/18 site-B low-rank skew factors (in/out; the rank sweep's
+  low-rank mismatch only).
 """
 from __future__ import annotations
 
@@ -81,6 +83,7 @@ def workload(key) -> Workload:
 # weight name -> seed stream
 WEIGHT_STREAMS = {"q": 4, "k": 5, "v": 6, "o": 7, "gate": 8, "up": 9, "down": 10, "proj": 4}
 SKEW_STREAMS = {("A", "in"): 1, ("A", "out"): 2, ("B", "in"): 13, ("B", "out"): 14}
+LOW_RANK_STREAMS = {("A", "in"): 15, ("A", "out"): 16, ("B", "in"): 17, ("B", "out"): 18}
 INPUT_STREAMS = {"o_in": 11, "down_in": 12}
 
 
