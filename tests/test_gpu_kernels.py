@@ -267,9 +267,11 @@ def test_qgemm_longest_k_with_extreme_accumulators(bits, n, N, K, ydt):
 
 
 @pytest.mark.parametrize("bits,n,N,K", [(4, 1000, 12320, 4096), (4, 2000, 22048, 1056), (3, 2000, 22048, 4096),
-                                         (4, 1800, 12224, 4096), (3, 1800, 12224, 1056)])
+                                         (4, 1800, 12224, 4096), (3, 1800, 12224, 1056),
+                                         # 256 x 128 tiles (int4 packed in LDS, 256-code k steps; int3 widened)
+                                         (4, 1900, 4064, 4128), (4, 2048, 4096, 11008), (3, 1900, 4064, 4128)])
 def test_qgemm_large_tiles_with_ragged_edges(bits, n, N, K):
-    """Shapes that take the 256 x 256 or 256 x 192 tiles, with partial tiles in tokens, channels and k.
+    """Shapes that take the 256 x 256, 256 x 192 or 256 x 128 tiles, with partial tiles in tokens, channels and k.
 
     The y-only launch (LDS-staged epilogue) must equal the launch that also
     writes the accumulators (direct epilogue); sampled blocks match the oracle.
@@ -291,7 +293,7 @@ def test_qgemm_large_tiles_with_ragged_edges(bits, n, N, K):
     torch.cuda.synchronize()
     assert torch.equal(y, y2)
     rows = np.unique(np.r_[0, 255, 256, n - 1, rng.choice(n, 40, replace=False)])
-    cols = np.unique(np.r_[0, 191, 192, 255, 256, N - 33, N - 1, rng.choice(N, 120, replace=False)])
+    cols = np.unique(np.r_[0, 127, 128, 191, 192, 255, 256, N - 33, N - 1, rng.choice(N, 120, replace=False)])
     acc_ref = online.gemm(qa[rows], qw[cols])
     acc_gpu = acc[torch.from_numpy(rows).cuda()][:, torch.from_numpy(cols).cuda()].cpu().numpy().astype(np.int64)
     assert np.array_equal(acc_gpu, acc_ref)
