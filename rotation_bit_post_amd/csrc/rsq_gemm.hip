@@ -15,13 +15,16 @@
 // step is permuted the same way for both operands, which leaves the dot
 // products unchanged.
 //
-// On the 256 x 128 tiles int4 codes instead go into LDS packed, as loaded,
-// in 256-code k steps: each 16-byte LDS read is one 32-code group, widened in
-// registers, whose low and high 8 bytes feed two multiplies (the same split
-// for both operands). Per code that halves the LDS writes, the LDS reads and
-// the barriers, at the cost of widening per wave instead of once per
-// workgroup; the narrow tile has the registers for it (measured on MI355X,
-// 2048 tokens: o 37.0 against 38.8 us, down 85.0 against 97.4 us).
+// On the 256 x 128 tiles and the decode-size 32 x 32 and 64 x 64 tiles, int4
+// codes instead go into LDS packed, as loaded, in 256-code k steps: each
+// 16-byte LDS read is one 32-code group, widened in registers, whose low and
+// high 8 bytes feed two multiplies (the same split for both operands). Per
+// code that halves the LDS writes, the LDS reads and the barriers (and the
+// k steps of a tile), at the cost of widening per wave instead of once per
+// workgroup; these tiles have the registers for it (measured on MI355X:
+// 2048 tokens, o 37.0 against 38.8 us, down 85.0 against 97.4 us; 64 tokens,
+// q|k|v 11.4 against 13.6 us). The 256 x 192 and 256 x 256 tiles gain
+// nothing from it and keep the widened form.
 //
 // Matrix-core roles: A = activations (rows = tokens), B = weights (columns =
 // output channels). The epilogue stages the bf16 tile in LDS and writes it
@@ -721,6 +724,10 @@ template <int BITS, typename YT>
 hipError_t launch_b(const uint8_t *a, const float *sa, int64_t n, const uint8_t *w, const float *sw, int64_t N,
                     int64_t K, void *y, int64_t ld_y, int32_t *acc_out, const void *res, int64_t ld_r, hipStream_t s) {
     const int64_t cus = device_cus();
+    // int4 on the 32 x 32, 64 x 64 and 256 x 128 tiles: packed in LDS (see the
+    // top of the file; e.g. 64 tokens, q|k|v: 11.4 against 13.6 us; 32 tokens,
+    // gate|up: 11.8 against 15.7 us); the wider tiles keep the widened form
+    constexpr int PK = BITS == 4 ? kInt4Raw : BITS;
     if constexpr (BITS == kFp4) {
         // the fp4 operands have no decode-size kernels of their own: narrow tiles
         if (n <= 32) return launch_t<BITS, 32, 32, 1, 1, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s);
@@ -752,13 +759,13 @@ hipError_t launch_b(const uint8_t *a, const float *sa, int64_t n, const uint8_t 
         }
         if (n <= 32) {
             if (gemv_wgs <= 2 * cus) return launch_gemv<BITS, 1, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s);
-            return launch_t<BITS, 32, 32, 1, 1, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s);
+            return launch_t<PK, 32, 32, 1, 1, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s);
         }
         if (n <= 64) {
             // 64 x 64 tiles: half the re-reads of the activation rows of 64 x 32
             // tiles (q|k|v at 64 tokens: 13.1 against 15.2 us; gate|up equal)
             if (gemv_wgs <= cus) return launch_gemv<BITS, 2, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s);
-            return launch_t<BITS, 64, 64, 2, 2, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s);
+            return launch_t<PK, 64, 64, 2, 2, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s);
         }
     }
     const int64_t mt = (n + 255) / 256;
@@ -776,9 +783,7 @@ hipError_t launch_b(const uint8_t *a, const float *sa, int64_t n, const uint8_t 
         return launch_t<BITS, 256, 256, 4, 2, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s);
     if (c192 < c128)
         return launch_t<BITS, 256, 192, 4, 2, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s);
-    // int4 on the 256 x 128 tiles: packed in LDS (see the top of the file)
-    constexpr int B128 = BITS == 4 ? kInt4Raw : BITS;
-    return launch_t<B128, 256, 128, 4, 2, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s);
+    return launch_t<PK, 256, 128, 4, 2, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s);
 }
 
 // ------------------------------------------------- int3 codes -> fp4 codes

@@ -198,6 +198,9 @@ GEMM_CASES = [  # bits, n, N, K, y dtype
     (4, 16, 22016, 4096, "bf16"), (3, 12, 4096, 11008, "bf16"), (4, 40, 2048, 4128, "f32"),
     # long k with the 3-step register ring (1 and 16 tokens, ragged last k step)
     (4, 1, 64, 8224, "f32"), (3, 16, 128, 16416, "bf16"),
+    # int4 packed in LDS on the decode-size tiles: 64 x 64 (50 tokens) and 32 x 32 (27 tokens),
+    # ragged channels and a partial 256-code k step
+    (4, 50, 8224, 4128, "bf16"), (4, 27, 16448, 1056, "f32"),
 ]
 
 
