@@ -7,7 +7,7 @@ import numpy as np
 import pytest
 
 import synth
-from oracle import prep
+from oracle import online, prep
 
 
 def require_gpu():
@@ -76,10 +76,50 @@ def rel_l2(a, b) -> float:
     return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
 
 
-def code_mismatch_ok(gpu_codes, ref_codes, max_frac=1e-4):
-    """Codes may differ only by one level, on at most max_frac of the elements."""
-    d = np.abs(np.asarray(gpu_codes, np.int64) - np.asarray(ref_codes, np.int64))
-    return int(d.max(initial=0)) <= 1 and float(np.mean(d != 0)) <= max_frac, int(np.sum(d != 0)), int(d.max(initial=0))
+def quant_input(x, norm: bool, eps: float = 1e-5, weight=None) -> np.ndarray:
+    """The quantiser's float32 input as the oracle forms it from x as stored:
+    its RMSNorm (x * inv) * w when norm is set, else x itself."""
+    if norm:
+        return online.rmsnorm(x, eps, weight)
+    return np.asarray(x, np.float64).astype(np.float32)
+
+
+def code_mismatch_ok(gpu_codes, ref_codes, a, scales, max_frac=1e-4, ulps=16):
+    """Codes may differ only at rounding ties of the per-token quantiser.
+
+    Every differing code must (1) differ by one level, (2) sit where a / s,
+    taken in float64 from the float32 quantiser input a (formed from the
+    GPU's own h') and the GPU's per-row scale s, lies within `ulps` float32
+    ulps of a half-integer - a tie that a last-bit difference in the row's
+    statistics can tip either way - and (3) the differing codes are at most
+    max_frac of all. Returns (ok, differing codes, largest level difference,
+    differing codes that are not at a tie).
+    """
+    g = np.asarray(gpu_codes, np.int64)
+    r = np.asarray(ref_codes, np.int64)
+    d = np.abs(g - r)
+    bad = np.nonzero(d)
+    nbad = int(bad[0].size)
+    dmax = int(d.max(initial=0))
+    if nbad == 0:
+        return True, 0, 0, 0
+    a64 = np.asarray(a, np.float32).astype(np.float64)
+    s64 = np.asarray(scales, np.float32).astype(np.float64).reshape(-1)
+    s_el = s64[bad[0]]
+    pos = s_el > 0                    # a zero row has s = 0 and admits no difference
+    t = a64[bad] / np.where(pos, s_el, 1.0)
+    dist = np.abs(t - (np.floor(t) + 0.5))
+    at_tie = pos & (dist <= ulps * float(np.finfo(np.float32).eps) * np.abs(t))
+    not_tie = int(np.sum(~at_tie))
+    ok = dmax <= 1 and not_tie == 0 and nbad / d.size <= max_frac
+    return ok, nbad, dmax, not_tie
+
+
+def bf16_rounding_error(h, U, M) -> float:
+    """Relative L2 distance of the oracle's bf16 corrected residual from its own
+    unrounded float64 value: the rounding the stored h' cannot avoid."""
+    exact = online.reproject(h, online.transform(online.project(h, U), M), U)
+    return rel_l2(online.correct(h, U, M, "bf16"), exact)
 
 
 def subspace_site(d, r, seed, eps=0.3):

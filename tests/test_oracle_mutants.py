@@ -114,3 +114,39 @@ def test_fp4_mistakes_are_caught(monkeypatch):
         return out.astype(np.uint8)
     monkeypatch.setattr(packing, "pack_fp4", twos)
     _expect_failure(T_on.test_fp4_packing_hand_worked_bytes)
+
+
+def test_site_b_reading_the_uncorrected_residual_is_caught(monkeypatch):
+    real = online.layer_linear_path
+
+    def bad(h, site_a, site_b, weights, o_in, down_in, h_dtype, bits, eps, y_dtype):
+        out = real(h, site_a, site_b, weights, o_in, down_in, h_dtype, bits, eps, y_dtype)
+        b = online.layer_fused(h, *site_b, h_dtype, bits, eps, *weights["gate_up"], y_dtype)  # h, not site A's h'
+        out["siteB"], out["gate_up"] = b, b["y"]
+        return out
+    monkeypatch.setattr(online, "layer_linear_path", bad)
+    _expect_failure(T_on.test_layer_linear_path_wires_each_linear_to_its_input)
+
+
+def test_linears_fed_the_wrong_inputs_are_caught(monkeypatch):
+    real = online.layer_linear_path
+
+    def bad(h, site_a, site_b, weights, o_in, down_in, h_dtype, bits, eps, y_dtype):
+        out = real(h, site_a, site_b, weights, o_in, down_in, h_dtype, bits, eps, y_dtype)
+        out["qkv"], out["gate_up"] = (online.qgemm_packed(out["siteB"]["codes"], out["siteB"]["scales"],
+                                                          *weights["qkv"], out["siteB"]["q"].shape[1], bits, y_dtype)[0],
+                                      out["gate_up"])
+        return out
+    monkeypatch.setattr(online, "layer_linear_path", bad)
+    _expect_failure(T_on.test_layer_linear_path_wires_each_linear_to_its_input)
+
+
+def test_quantising_the_uncorrected_residual_is_caught(monkeypatch):
+    def bad(h, u, m, h_dtype, bits, eps, w_codes, w_scales, y_dtype, norm_weight=None):
+        hp = online.correct(h, u, m, h_dtype)
+        codes, scales, q = online.quant_act_packed(h, bits, True, eps, norm_weight)   # h instead of h'
+        y, acc = online.qgemm_packed(codes, scales, w_codes, w_scales, np.asarray(h).shape[1], bits, y_dtype)
+        return {"h_out": hp, "codes": codes, "scales": scales, "q": q, "y": y, "acc": acc}
+    monkeypatch.setattr(online, "layer_fused", bad)
+    _expect_failure(T_on.test_layer_fused_with_a_quarter_turn_site)
+    _expect_failure(T_on.test_layer_linear_path_wires_each_linear_to_its_input)

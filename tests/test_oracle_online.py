@@ -453,3 +453,91 @@ def test_fp4_rejects_codes_outside_the_3bit_range():
         packing.pack_fp4(np.full((1, 32), -4))
     with pytest.raises(ValueError):
         packing.unpack_fp4(np.full((1, 16), 0x44, np.uint8), 32)   # 2.0 -> code 4
+
+
+# ------------------------------------------------ one site and its linear, M != 0
+def _quarter_turn_site(d, i=0, j=1):
+    """The site of a quarter turn in the plane of coordinates i and j: U = [e_i e_j],
+    M = R - I_2 with R the 90-degree rotation. For a row h its exact correction is
+    h with (h_i, h_j) replaced by (h_j, -h_i); every float64 step is exact."""
+    u = np.zeros((d, 2), np.float32)
+    u[i, 0] = u[j, 1] = 1.0
+    rot = np.array([[0.0, -1.0], [1.0, 0.0]])
+    return u, (rot - np.eye(2)).astype(np.float32)
+
+
+def _turned(x, i=0, j=1):
+    y = np.array(x, copy=True)
+    y[:, i], y[:, j] = x[:, j], -x[:, i]
+    return y
+
+
+def test_layer_fused_with_a_quarter_turn_site():
+    # zh 2.2 steps 1-3 with a non-identity M whose result is known exactly; the
+    # norm and the quantiser are invariant under the turn (same multiset of
+    # magnitudes), so the codes are the turned codes of h, and the linear
+    # equals the plain linear with the weight's columns 0 and 1 turned back.
+    rng = np.random.default_rng(60)
+    d, n, nout, bits = 64, 7, 32, 4
+    h = rng.standard_normal((n, d)) * 3
+    h[:, 5] *= 40                                              # an outlier channel
+    h = _bf16_exact(h)
+    u, m = _quarter_turn_site(d)
+    w = (rng.standard_normal((nout, d)) * 0.02).astype(np.float32)
+    qw, sw = prep.quantize_weight(w, bits)
+    out = online.layer_fused(h, u, m, "bf16", bits, 1e-5, packing.pack(qw, bits), sw, "bf16")
+    assert np.array_equal(out["h_out"], _turned(h))
+    assert not np.array_equal(out["h_out"], h)
+    q_plain, s_plain = online.quant_act(h, bits, True, 1e-5)
+    assert np.array_equal(out["q"], _turned(q_plain))
+    assert np.array_equal(out["scales"], s_plain)
+    # sum_k q'_k w_k = q1 w0 - q0 w1 + ... = sum_k q_k w''_k with w''_0 = -w_1, w''_1 = w_0
+    qw_back = np.array(qw, copy=True)
+    qw_back[:, 0], qw_back[:, 1] = -qw[:, 1], qw[:, 0]
+    y_plain, acc_plain = online.qgemm_packed(packing.pack(q_plain, bits), s_plain, packing.pack(qw_back, bits), sw,
+                                             d, bits, "bf16")
+    assert np.array_equal(out["acc"], acc_plain)
+    assert np.array_equal(out["y"], y_plain)
+
+
+def _constant_linear(nout, k, code, bits):
+    """Packed weight codes all equal to `code`, unit channel scales."""
+    return packing.pack(np.full((nout, k), code, np.int64), bits), np.ones(nout, np.float32)
+
+
+def test_layer_linear_path_wires_each_linear_to_its_input():
+    # The path of one layer: site A corrects h and feeds q|k|v, site B corrects
+    # site A's h' and feeds gate|up, o reads the o_proj input and down the
+    # down_proj input. Both sites are quarter turns (in different planes), so
+    # each corrected residual and its codes are known exactly; constant weights
+    # turn each output into a closed form of its input's codes (a row sum),
+    # different for every linear, so any miswiring shows.
+    rng = np.random.default_rng(61)
+    d, f, n, bits = 64, 96, 5, 4
+    h = _bf16_exact(rng.standard_normal((n, d)) * 2)
+    o_in = _bf16_exact(rng.standard_normal((n, d)))
+    down_in = _bf16_exact(rng.standard_normal((n, f)))
+    site_a, site_b = _quarter_turn_site(d, 0, 1), _quarter_turn_site(d, 2, 3)
+    weights = {"qkv": _constant_linear(3 * d, d, 1, bits), "o": _constant_linear(d, d, 2, bits),
+               "gate_up": _constant_linear(2 * f, d, -1, bits), "down": _constant_linear(d, f, 3, bits)}
+    out = online.layer_linear_path(h, site_a, site_b, weights, o_in, down_in, "bf16", bits, 1e-5, "f32")
+    h_a, h_b = _turned(h, 0, 1), _turned(_turned(h, 0, 1), 2, 3)
+    assert np.array_equal(out["siteA"]["h_out"], h_a)
+    assert np.array_equal(out["siteB"]["h_out"], h_b)            # site B's input is site A's h'
+    q_plain, s_plain = online.quant_act(h, bits, True, 1e-5)      # the turns keep the norm and the scale
+    qa, sa = out["siteA"]["q"], out["siteA"]["scales"]
+    qb, sb = out["siteB"]["q"], out["siteB"]["scales"]
+    assert np.array_equal(qa, _turned(q_plain, 0, 1)) and np.array_equal(sa, s_plain)
+    assert np.array_equal(qb, _turned(_turned(q_plain, 0, 1), 2, 3)) and np.array_equal(sb, s_plain)
+
+    def row_sum_output(q, s, code, nout):
+        v = (q.sum(axis=1).astype(np.float32) * code) * s       # (float32(acc) * s_a) * s_w with s_w = 1
+        return np.repeat(v[:, None].astype(np.float32), nout, axis=1)
+    qo, so = online.quant_act(o_in, bits, False)
+    qd, sd = online.quant_act(down_in, bits, False)
+    assert np.array_equal(out["qkv"], row_sum_output(qa, sa, 1, 3 * d))
+    assert np.array_equal(out["gate_up"], row_sum_output(qb, sb, -1, 2 * f))
+    assert np.array_equal(out["o"], row_sum_output(qo, so, 2, d))
+    assert np.array_equal(out["down"], row_sum_output(qd, sd, 3, d))
+    # the row sums of the two sites' codes differ, so swapping their linears would show
+    assert not np.array_equal(qa.sum(axis=1), qb.sum(axis=1))
