@@ -57,6 +57,8 @@ def parse():
                    help="the rank sweep's site mismatch: the workload's (dense) or one with T - I of rank <= 64")
     p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                    help="only run a plain device copy of MIB MiB (calibrates rocprofv3 byte counters) and exit")
+    p.add_argument("--mha", action="store_true", help="all-D x D q/k/v projections instead of the GQA shapes")
+    p.add_argument("--no-decode", action="store_true", help="skip the decode-size leg (1, 8 and 64 tokens)")
     return p.parse_args()
 
 
@@ -75,6 +77,65 @@ def copy_probe(mib: int) -> None:
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_probe_bytes_read": nbytes, "copy_probe_bytes_written": nbytes, "dispatches": 3}))
+
+
+def capture(fns, reps: int = 1):
+    """One HIP graph of `reps` passes over the launches fns (each launched once
+    outside the capture first); the launches allocate nothing and set no memory."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for fn in fns:
+            fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(reps):
+            for fn in fns:
+                fn()
+    return graph
+
+
+def replay_ms(graphs, iters: int, stream) -> float:
+    """Mean time of one replay, the graphs replayed in turn (events on the stream around all of them)."""
+    import torch
+    for i in range(max(3, len(graphs))):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(iters):
+        graphs[i % len(graphs)].replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / iters
+
+
+def copy_ceiling(nbytes: int, iters: int = 50):
+    """Time of a plain device copy that moves nbytes (half read, half written), cold: the
+    copies rotate over more than twice the 256 MB Infinity Cache. The practical ceiling of a
+    stage that streams the same bytes once."""
+    import torch
+    half = max(nbytes // 2 // 16 * 16, 16)
+    nbuf = max(2, int((600 << 20) // (2 * half)) + 1)
+    src = [torch.ones(half, dtype=torch.uint8, device="cuda") for _ in range(nbuf)]
+    dst = [torch.empty(half, dtype=torch.uint8, device="cuda") for _ in range(nbuf)]
+    stream = torch.cuda.current_stream()
+    for i in range(nbuf):
+        dst[i].copy_(src[i])
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(iters):
+        dst[i % nbuf].copy_(src[i % nbuf])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / iters
+    del src, dst
+    torch.cuda.empty_cache()
+    return ms
 
 
 def _time_ms(fn, iters: int, stream) -> float:
@@ -266,6 +327,61 @@ def cpu_baseline(path, n_sample: int, min_s: float = 10.0):
                       f"float64 numpy; {passes} pass(es) in {dt:.1f} s wall"}
 
 
+def decode_leg(sites, ns=(1, 8, 64), copies: int = 3, iters: int = 100):
+    """The decode workload (the same layer at 1, 8 and 64 tokens, the prefill workload's
+    sites, weights and leading residual rows): one step, and each stage, as replayed HIP
+    graphs - an eager decode step is bound by the host's launch rate, not the GPU. Three
+    copies of every buffer rotate (more than the 256 MB Infinity Cache of weights)."""
+    import torch
+    import synth
+    from rotation_bit_post_amd.path import LayerPath
+    stream = torch.cuda.current_stream()
+    out = {}
+    for n in ns:
+        progress(f"decode leg: {n} token(s)")
+        base = LayerPath.build(synth.LLAMA2_7B_DECODE, n=n, sites=sites)
+        paths = [base] + [base.clone() for _ in range(copies - 1)]
+        # the step as a graph, checked against the eager step first
+        base.step()
+        torch.cuda.synchronize()
+        ref = {k: v.clone() for k, v in base.outputs().items()}
+        for v in base.outputs().values():
+            v.zero_()
+        graphs = [p.capture() for p in paths]
+        for v in base.outputs().values():
+            v.zero_()
+        graphs[0].replay()
+        torch.cuda.synchronize()
+        same = all(torch.equal(v, ref[k]) for k, v in base.outputs().items())
+        ms_step = replay_ms(graphs, iters, stream)
+        # each stage alone: a graph of 10 launches per buffer copy
+        stages = {}
+        gemm_bytes = gemm_ms = 0.0
+        names = [nm for nm, _, _ in base.stages()]
+        for j, nm in enumerate(names):
+            g = [capture([p.stages()[j][2]], reps=10) for p in paths]
+            ms = replay_ms(g, max(10, iters // 5), stream) / 10
+            byts, ops = base.stage_work(nm)
+            stages[nm] = {"ms": round(ms, 5), "alg_bytes": byts, "hbm_frac": round(byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+            if ops:
+                gemm_bytes += byts
+                gemm_ms += ms
+            del g
+        out[str(n)] = {
+            "ms_per_step": round(ms_step, 5),
+            "tokens_per_s": round(n / (ms_step * 1e-3), 1),
+            "graph_outputs_identical": same,
+            "gemm_hbm_frac": round(gemm_bytes / (gemm_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "stages": stages,
+        }
+        del paths, graphs, base
+        torch.cuda.empty_cache()
+    out["note"] = ("decode-size batches of the same layer (llama2-7b shapes, W4A4), steps and stages replayed as HIP "
+                   "graphs; stage times include the graph's per-launch dispatch; hbm_frac = algorithmic bytes / time / "
+                   "8 TB/s")
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -284,7 +400,7 @@ def main():
 
     t_build = time.perf_counter()
     progress(f"building workload {args.workload} (sites, weights, inputs)")
-    base = LayerPath.build(args.workload, keep_mismatch=not args.no_dense, prep=args.prep)
+    base = LayerPath.build(args.workload, keep_mismatch=not args.no_dense, prep=args.prep, gqa=not args.mha)
     copies = [base] + [base.clone() for _ in range(args.copies - 1)]
     torch.cuda.synchronize()
     t_build = time.perf_counter() - t_build
@@ -418,10 +534,43 @@ def main():
             gemm_launches += 1
         stages_out[nm] = rec
 
+    # practical ceiling of the memory-bound stages: a plain device copy moving the same bytes
+    progress("copy ceilings of the memory-bound stages")
+    ceil_ms = {}
+    for nm in names:
+        if kinds[nm] in ("site", "quant"):
+            byts = stages_out[nm]["alg_bytes"]
+            if byts not in ceil_ms:
+                ceil_ms[byts] = copy_ceiling(byts)
+            stages_out[nm]["copy_ms"] = round(ceil_ms[byts], 5)
+            stages_out[nm]["copy_hbm_frac"] = round(byts / (ceil_ms[byts] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+            stages_out[nm]["frac_of_copy"] = round(ceil_ms[byts] / stages_out[nm]["ms"], 4)
+
     src_hash = kernel_source_hash()
-    achieved = gemm_ops / (gemm_ms * 1e-3) / 1e12
     traffic = measured_traffic(cfg.name, src_hash)
     value = n / (ms_per_step * 1e-3)
+    decode_sized = n <= 64
+    if decode_sized:
+        # a few tokens: the GEMMs stream their weights once, so HBM bounds them
+        gemm_bytes = sum(stages_out[nm]["alg_bytes"] for nm in names if kinds[nm] == "gemm")
+        achieved = gemm_bytes / (gemm_ms * 1e-3) / 1e9
+        roofline = {"kernel": "the four quantised-linear launches of a step (weights streamed once)", "bound": "hbm",
+                    "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                    "avg_launch_ms": round(gemm_ms / max(gemm_launches, 1), 5)}
+    else:
+        achieved = gemm_ops / (gemm_ms * 1e-3) / 1e12
+        roofline = {
+            "kernel": ("qgemm_kernel (3-bit codes as fp4 on v_mfma_scale_f32_32x32x64_f8f6f4)" if base.fp4 else
+                       f"qgemm_kernel (int{cfg.bits} codes on v_mfma_i32_32x32x32_i8)") + ", all 4 launches of a step",
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": gemm_peak,
+            "unit": "TOP/s",
+            "frac": round(achieved / gemm_peak, 4),
+            "traffic": traffic,
+            "avg_launch_ms": round(gemm_ms / max(gemm_launches, 1), 5),
+        }
     out = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -442,18 +591,9 @@ def main():
                         f"quantisations + GEMMs qkv {base.linears['qkv'].N}x{cfg.D}, o {cfg.D}x{cfg.D}, "
                         f"gate|up {base.linears['gate_up'].N}x{cfg.D}, down {cfg.D}x{cfg.F}",
             "tokens": n, "D": cfg.D, "ffn": cfg.F, "r": base.r, "bits": cfg.bits, "buffer_copies": len(copies),
+            "qkv": "all D x D (MHA)" if args.mha else "GQA where the model has it",
         },
-        "roofline": {
-            "kernel": ("qgemm_kernel (3-bit codes as fp4 on v_mfma_scale_f32_32x32x64_f8f6f4)" if base.fp4 else
-                       f"qgemm_kernel (int{cfg.bits} codes on v_mfma_i32_32x32x32_i8)") + ", all 4 launches of a step",
-            "bound": "mfma",
-            "achieved": round(achieved, 2),
-            "peak": gemm_peak,
-            "unit": "TOP/s",
-            "frac": round(achieved / gemm_peak, 4),
-            "traffic": traffic,
-            "avg_launch_ms": round(gemm_ms / max(gemm_launches, 1), 5),
-        },
+        "roofline": roofline,
         "stages": stages_out,
         "correction_overhead": {
             "ms_per_step_correction_off": round(ms_off, 5),
@@ -486,6 +626,9 @@ def main():
     if not args.no_dense and "A" in base.mismatch:
         progress("dense h T comparator")
         out["dense_T_comparator"] = dense_comparator(base)
+    if not args.no_decode and cfg.name == "llama2-7b-prefill-w4a4":
+        sites = {w: (st.U.cpu().numpy(), st.M.cpu().numpy()) for w, st in base.sites.items()}
+        out["decode"] = decode_leg(sites)
     if not args.no_cpu_baseline:
         progress(f"CPU oracle on a {min(args.cpu_sample, n)}-token sample")
         out["cpu_baseline"] = cpu_baseline(base, min(args.cpu_sample, n))

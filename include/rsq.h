@@ -10,6 +10,15 @@
  *  - Memory: the caller owns all memory. Pointers named "host" are host
  *    pointers; every other pointer is a device pointer on the current HIP
  *    device, at least 16-byte aligned. The library allocates nothing.
+ *  - Workspace: the entry points that take `workspace, workspace_bytes` may
+ *    need device scratch (partial sums and arrival counters of work split
+ *    over workgroups), sized by the matching rsq_*_workspace_bytes query for
+ *    the same sizes. A query result of 0 means NULL, 0 may be passed. The
+ *    workspace must be zero-filled before its first use (once, e.g. right
+ *    after allocation); every call leaves its counters at zero again, so a
+ *    workspace serves any number of later calls without clearing. Calls that
+ *    share a workspace must not run concurrently (enqueue them on one
+ *    stream). Too small a workspace is RSQ_ERR_WORKSPACE.
  *  - Execution: work is enqueued on `stream` (a hipStream_t; NULL is the
  *    null stream) and the call returns without waiting. Device faults show
  *    at the caller's next synchronisation.
@@ -56,7 +65,7 @@ typedef enum {
     RSQ_OK = 0,
     RSQ_ERR_INVALID_ARG = 1,   /* null pointer, negative or inconsistent size, misalignment */
     RSQ_ERR_UNSUPPORTED = 2,   /* valid but outside what the kernels handle (e.g. r > 64) */
-    RSQ_ERR_WORKSPACE = 3,     /* reserved: no entry point takes a workspace */
+    RSQ_ERR_WORKSPACE = 3,     /* workspace NULL, misaligned or smaller than its query */
     RSQ_ERR_HIP = 4            /* the HIP runtime refused a launch or a query */
 } rsq_status;
 
@@ -84,6 +93,15 @@ const char *rsq_last_error(void);
 /* Bytes of one packed row of k codes (0 if k or bits is invalid; bits 3,
  * 4 or 3 | RSQ_FP4). */
 size_t rsq_packed_row_bytes(int64_t k, int bits);
+
+/* Workspace bytes (see Conventions) of rsq_qgemm, rsq_qgemm_residual and
+ * rsq_qgemm_fp4 (bits 3 | RSQ_FP4) for n tokens, n_out channels and k codes;
+ * of rsq_correct_quant for n tokens of width d; of rsq_layer_fused for both
+ * its stages. 0 if no kernel for these sizes needs scratch, or if a size is
+ * invalid (the call then reports the invalid size). */
+size_t rsq_qgemm_workspace_bytes(int64_t n, int64_t n_out, int64_t k, int bits);
+size_t rsq_correct_workspace_bytes(int64_t n, int64_t d);
+size_t rsq_layer_workspace_bytes(int64_t n, int64_t d, int64_t n_out, int bits);
 
 /*
  * Correction site (offline, once per model). The pages apply, per residual
@@ -144,7 +162,8 @@ rsq_status rsq_quant_act(const void *x, int x_dtype, int64_t n, int64_t k, int64
  */
 rsq_status rsq_correct_quant(const void *h_in, void *h_out, int h_dtype, int64_t n, int64_t d,
                              const void *site, int r, const float *norm_w, float eps, int bits,
-                             uint8_t *codes, float *scales, void *stream);
+                             uint8_t *codes, float *scales, void *workspace, size_t workspace_bytes,
+                             void *stream);
 
 /*
  * Quantised linear with per-token and per-channel dequantisation (W4A4 /
@@ -158,7 +177,7 @@ rsq_status rsq_correct_quant(const void *h_in, void *h_out, int h_dtype, int64_t
 rsq_status rsq_qgemm(const uint8_t *a_codes, const float *a_scales, int64_t n,
                      const uint8_t *w_codes, const float *w_scales, int64_t n_out,
                      int64_t k, int bits, void *y, int y_dtype, int64_t ld_y,
-                     int32_t *acc_out, void *stream);
+                     int32_t *acc_out, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Quantised linear plus a residual: the residual adds around the attention
@@ -172,7 +191,8 @@ rsq_status rsq_qgemm(const uint8_t *a_codes, const float *a_scales, int64_t n,
 rsq_status rsq_qgemm_residual(const uint8_t *a_codes, const float *a_scales, int64_t n,
                               const uint8_t *w_codes, const float *w_scales, int64_t n_out,
                               int64_t k, int bits, const void *residual, int64_t ld_r,
-                              void *y, int y_dtype, int64_t ld_y, void *stream);
+                              void *y, int y_dtype, int64_t ld_y, void *workspace,
+                              size_t workspace_bytes, void *stream);
 
 /*
  * 3-bit codes in another layout for the fp4 matrix cores: each of `rows`
@@ -199,7 +219,8 @@ rsq_status rsq_codes_to_fp4(const uint8_t *codes, int64_t rows, int64_t k, uint8
  */
 rsq_status rsq_qgemm_fp4(const uint8_t *a_fp4, const float *a_scales, int64_t n, const uint8_t *w_fp4,
                          const float *w_scales, int64_t n_out, int64_t k, const void *residual, int64_t ld_r, void *y,
-                         int y_dtype, int64_t ld_y, int32_t *acc_out, void *stream);
+                         int y_dtype, int64_t ld_y, int32_t *acc_out, void *workspace, size_t workspace_bytes,
+                         void *stream);
 
 /*
  * One correction site feeding its quantised linear: rsq_correct_quant then
@@ -209,7 +230,7 @@ rsq_status rsq_layer_fused(const void *h_in, void *h_out, int h_dtype, int64_t n
                            const void *site, int r, const float *norm_w, float eps, int bits,
                            uint8_t *codes, float *scales,
                            const uint8_t *w_codes, const float *w_scales, int64_t n_out,
-                           void *y, int y_dtype, void *stream);
+                           void *y, int y_dtype, void *workspace, size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

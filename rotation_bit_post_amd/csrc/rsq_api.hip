@@ -55,6 +55,25 @@ rsq_status check_bits(int bits) {
 // The launchers' code format for a checked `bits`.
 int code_format(int bits) { return bits == (3 | RSQ_FP4) ? rsq::kFp4 : bits; }
 
+// A workspace of `have` bytes at ws for a launch that needs `need`.
+rsq_status check_workspace(size_t need, const void *ws, size_t have) {
+    if (need == 0) return RSQ_OK;
+    RSQ_CHECK(ws != nullptr && aligned16(ws), RSQ_ERR_WORKSPACE,
+              "a workspace of %zu bytes is needed (non-null, 16-byte aligned)", need);
+    RSQ_CHECK(have >= need, RSQ_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu bytes needed", have, need);
+    return RSQ_OK;
+}
+
+rsq_status check_norm_w(const float *norm_w) {
+    RSQ_CHECK(norm_w == nullptr || aligned16(norm_w), RSQ_ERR_INVALID_ARG, "norm_w must be 16-byte aligned");
+    return RSQ_OK;
+}
+
+bool gemm_sizes_ok(int64_t n, int64_t n_out, int64_t k) {
+    return n >= 0 && n <= 0x7fffffff && n_out > 0 && n_out % 32 == 0 && n_out <= 0x7fffffff && k > 0 &&
+           k % 32 == 0 && k <= 65536;
+}
+
 rsq_status check_correct_args(const void *h_in, const void *h_out, int h_dtype, int64_t n, int64_t d, int64_t ld_h,
                               const void *site, int r) {
     RSQ_CHECK(dtype_ok(h_dtype), RSQ_ERR_INVALID_ARG, "h_dtype = %d is not RSQ_F32 or RSQ_BF16", h_dtype);
@@ -131,7 +150,7 @@ rsq_status check_residual(int64_t n, int64_t n_out, int y_dtype, const void *res
 
 extern "C" {
 
-int rsq_version(void) { return 100; }
+int rsq_version(void) { return 200; }
 
 const char *rsq_status_str(int status) {
     switch (status) {
@@ -151,6 +170,22 @@ size_t rsq_packed_row_bytes(int64_t k, int bits) {
     if (bits == 4 || bits == (3 | RSQ_FP4)) return static_cast<size_t>(k) / 2;
     if (bits == 3) return static_cast<size_t>(k) * 3 / 8;
     return 0;
+}
+
+size_t rsq_qgemm_workspace_bytes(int64_t n, int64_t n_out, int64_t k, int bits) {
+    if (!gemm_sizes_ok(n, n_out, k) || rsq_packed_row_bytes(k, bits) == 0 || n == 0) return 0;
+    return rsq::qgemm_workspace_bytes(n, n_out, k, code_format(bits));
+}
+
+size_t rsq_correct_workspace_bytes(int64_t n, int64_t d) {
+    int nw = 0, cpw = 0;
+    if (n <= 0 || n > 0x7fffffff || !rsq::correct_geometry(d, false, &nw, &cpw)) return 0;
+    return rsq::correct_workspace_bytes(n, d);
+}
+
+size_t rsq_layer_workspace_bytes(int64_t n, int64_t d, int64_t n_out, int bits) {
+    const size_t a = rsq_correct_workspace_bytes(n, d), b = rsq_qgemm_workspace_bytes(n, n_out, d, bits);
+    return a > b ? a : b;
 }
 
 size_t rsq_site_bytes(int64_t d, int r) {
@@ -174,7 +209,7 @@ rsq_status rsq_subspace_correct(const void *h_in, void *h_out, int h_dtype, int6
     rsq_status st = check_correct_args(h_in, h_out, h_dtype, n, d, ld_h, site, r);
     if (st != RSQ_OK || n == 0) return st;
     return hip_status(rsq::launch_correct(h_in, h_out, h_dtype, n, static_cast<int>(d), ld_h, site, r, false,
-                                          nullptr, 0.0f, 4, nullptr, nullptr, static_cast<hipStream_t>(stream)),
+                                          nullptr, 0.0f, 4, nullptr, nullptr, nullptr, static_cast<hipStream_t>(stream)),
                       "rsq_subspace_correct launch");
 }
 
@@ -191,6 +226,8 @@ rsq_status rsq_quant_act(const void *x, int x_dtype, int64_t n, int64_t k, int64
     RSQ_CHECK(!(flags & RSQ_QA_RMSNORM) || eps >= 0.0f, RSQ_ERR_INVALID_ARG, "eps must be >= 0");
     RSQ_CHECK(n <= 0x7fffffff, RSQ_ERR_UNSUPPORTED, "n too large");
     rsq_status st = check_quant_out(n, k, bits, codes, scales);
+    if (st != RSQ_OK) return st;
+    st = check_norm_w(norm_w);
     if (st != RSQ_OK || n == 0) return st;
     RSQ_CHECK(x != nullptr && aligned16(x), RSQ_ERR_INVALID_ARG, "x must be non-null and 16-byte aligned");
     return hip_status(rsq::launch_quant(x, x_dtype, n, static_cast<int>(k), ld_x, (flags & RSQ_QA_RMSNORM) != 0,
@@ -200,35 +237,44 @@ rsq_status rsq_quant_act(const void *x, int x_dtype, int64_t n, int64_t k, int64
 
 rsq_status rsq_correct_quant(const void *h_in, void *h_out, int h_dtype, int64_t n, int64_t d, const void *site,
                              int r, const float *norm_w, float eps, int bits, uint8_t *codes, float *scales,
-                             void *stream) {
+                             void *workspace, size_t workspace_bytes, void *stream) {
     g_last_error[0] = 0;
     rsq_status st = check_correct_args(h_in, h_out, h_dtype, n, d, d, site, r);
     if (st != RSQ_OK) return st;
     RSQ_CHECK(eps >= 0.0f, RSQ_ERR_INVALID_ARG, "eps must be >= 0");
     st = check_quant_out(n, d, bits, codes, scales);
+    if (st != RSQ_OK) return st;
+    st = check_norm_w(norm_w);
     if (st != RSQ_OK || n == 0) return st;
+    st = check_workspace(rsq::correct_workspace_bytes(n, d), workspace, workspace_bytes);
+    if (st != RSQ_OK) return st;
     return hip_status(rsq::launch_correct(h_in, h_out, h_dtype, n, static_cast<int>(d), d, site, r, true, norm_w,
-                                          eps, code_format(bits), codes, scales, static_cast<hipStream_t>(stream)),
+                                          eps, code_format(bits), codes, scales, workspace,
+                                          static_cast<hipStream_t>(stream)),
                       "rsq_correct_quant launch");
 }
 
 rsq_status rsq_qgemm(const uint8_t *a_codes, const float *a_scales, int64_t n, const uint8_t *w_codes,
                      const float *w_scales, int64_t n_out, int64_t k, int bits, void *y, int y_dtype, int64_t ld_y,
-                     int32_t *acc_out, void *stream) {
+                     int32_t *acc_out, void *workspace, size_t workspace_bytes, void *stream) {
     g_last_error[0] = 0;
     rsq_status st = check_bits(bits);
     if (st != RSQ_OK) return st;
     st = check_gemm(n, n_out, k, y_dtype, ld_y, a_codes, a_scales, w_codes, w_scales, y);
     if (st != RSQ_OK || n == 0) return st;
     RSQ_CHECK(acc_out == nullptr || aligned16(acc_out), RSQ_ERR_INVALID_ARG, "acc_out must be 16-byte aligned");
+    st = check_workspace(rsq::qgemm_workspace_bytes(n, n_out, k, code_format(bits)), workspace, workspace_bytes);
+    if (st != RSQ_OK) return st;
     return hip_status(rsq::launch_qgemm(a_codes, a_scales, n, w_codes, w_scales, n_out, k, code_format(bits), y,
-                                        y_dtype, ld_y, acc_out, nullptr, 0, static_cast<hipStream_t>(stream)),
+                                        y_dtype, ld_y, acc_out, nullptr, 0, workspace,
+                                        static_cast<hipStream_t>(stream)),
                       "rsq_qgemm launch");
 }
 
 rsq_status rsq_qgemm_residual(const uint8_t *a_codes, const float *a_scales, int64_t n, const uint8_t *w_codes,
                               const float *w_scales, int64_t n_out, int64_t k, int bits, const void *residual,
-                              int64_t ld_r, void *y, int y_dtype, int64_t ld_y, void *stream) {
+                              int64_t ld_r, void *y, int y_dtype, int64_t ld_y, void *workspace,
+                              size_t workspace_bytes, void *stream) {
     g_last_error[0] = 0;
     rsq_status st = check_bits(bits);
     if (st != RSQ_OK) return st;
@@ -236,8 +282,11 @@ rsq_status rsq_qgemm_residual(const uint8_t *a_codes, const float *a_scales, int
     if (st != RSQ_OK) return st;
     st = check_residual(n, n_out, y_dtype, residual, ld_r, y, ld_y);
     if (st != RSQ_OK || n == 0) return st;
+    st = check_workspace(rsq::qgemm_workspace_bytes(n, n_out, k, code_format(bits)), workspace, workspace_bytes);
+    if (st != RSQ_OK) return st;
     return hip_status(rsq::launch_qgemm(a_codes, a_scales, n, w_codes, w_scales, n_out, k, code_format(bits), y,
-                                        y_dtype, ld_y, nullptr, residual, ld_r, static_cast<hipStream_t>(stream)),
+                                        y_dtype, ld_y, nullptr, residual, ld_r, workspace,
+                                        static_cast<hipStream_t>(stream)),
                       "rsq_qgemm_residual launch");
 }
 
@@ -259,7 +308,8 @@ rsq_status rsq_codes_to_fp4(const uint8_t *codes, int64_t rows, int64_t k, uint8
 
 rsq_status rsq_qgemm_fp4(const uint8_t *a_fp4, const float *a_scales, int64_t n, const uint8_t *w_fp4,
                          const float *w_scales, int64_t n_out, int64_t k, const void *residual, int64_t ld_r, void *y,
-                         int y_dtype, int64_t ld_y, int32_t *acc_out, void *stream) {
+                         int y_dtype, int64_t ld_y, int32_t *acc_out, void *workspace, size_t workspace_bytes,
+                         void *stream) {
     g_last_error[0] = 0;
     rsq_status st = check_gemm(n, n_out, k, y_dtype, ld_y, a_fp4, a_scales, w_fp4, w_scales, y);
     if (st != RSQ_OK) return st;
@@ -269,8 +319,10 @@ rsq_status rsq_qgemm_fp4(const uint8_t *a_fp4, const float *a_scales, int64_t n,
     }
     if (n == 0) return RSQ_OK;
     RSQ_CHECK(acc_out == nullptr || aligned16(acc_out), RSQ_ERR_INVALID_ARG, "acc_out must be 16-byte aligned");
+    st = check_workspace(rsq::qgemm_workspace_bytes(n, n_out, k, rsq::kFp4), workspace, workspace_bytes);
+    if (st != RSQ_OK) return st;
     return hip_status(rsq::launch_qgemm(a_fp4, a_scales, n, w_fp4, w_scales, n_out, k, rsq::kFp4, y, y_dtype, ld_y,
-                                        acc_out, residual, residual != nullptr ? ld_r : 0,
+                                        acc_out, residual, residual != nullptr ? ld_r : 0, workspace,
                                         static_cast<hipStream_t>(stream)),
                       "rsq_qgemm_fp4 launch");
 }
@@ -278,11 +330,13 @@ rsq_status rsq_qgemm_fp4(const uint8_t *a_fp4, const float *a_scales, int64_t n,
 rsq_status rsq_layer_fused(const void *h_in, void *h_out, int h_dtype, int64_t n, int64_t d, const void *site, int r,
                            const float *norm_w, float eps, int bits, uint8_t *codes, float *scales,
                            const uint8_t *w_codes, const float *w_scales, int64_t n_out, void *y, int y_dtype,
-                           void *stream) {
+                           void *workspace, size_t workspace_bytes, void *stream) {
     g_last_error[0] = 0;
     rsq_status st = check_correct_args(h_in, h_out, h_dtype, n, d, d, site, r);
     if (st != RSQ_OK) return st;
     st = check_quant_out(n, d, bits, codes, scales);
+    if (st != RSQ_OK) return st;
+    st = check_norm_w(norm_w);
     if (st != RSQ_OK) return st;
     RSQ_CHECK(eps >= 0.0f, RSQ_ERR_INVALID_ARG, "eps must be >= 0");
     RSQ_CHECK(dtype_ok(y_dtype), RSQ_ERR_INVALID_ARG, "y_dtype = %d is not RSQ_F32 or RSQ_BF16", y_dtype);
@@ -291,13 +345,18 @@ rsq_status rsq_layer_fused(const void *h_in, void *h_out, int h_dtype, int64_t n
     if (n == 0) return RSQ_OK;
     RSQ_CHECK(w_codes && w_scales && y, RSQ_ERR_INVALID_ARG, "null pointer (w_codes, w_scales or y)");
     RSQ_CHECK(aligned16(w_codes) && aligned16(w_scales) && aligned16(y), RSQ_ERR_INVALID_ARG, "operands must be 16-byte aligned");
+    // the two stages run one after the other on the stream: one workspace serves both
+    const size_t need_c = rsq::correct_workspace_bytes(n, d);
+    const size_t need_g = rsq::qgemm_workspace_bytes(n, n_out, d, code_format(bits));
+    st = check_workspace(need_c > need_g ? need_c : need_g, workspace, workspace_bytes);
+    if (st != RSQ_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     st = hip_status(rsq::launch_correct(h_in, h_out, h_dtype, n, static_cast<int>(d), d, site, r, true, norm_w, eps,
-                                        code_format(bits), codes, scales, s),
+                                        code_format(bits), codes, scales, workspace, s),
                     "rsq_layer_fused correction launch");
     if (st != RSQ_OK) return st;
     return hip_status(rsq::launch_qgemm(codes, scales, n, w_codes, w_scales, n_out, d, code_format(bits), y, y_dtype,
-                                        n_out, nullptr, nullptr, 0, s),
+                                        n_out, nullptr, nullptr, 0, workspace, s),
                       "rsq_layer_fused GEMM launch");
 }
 

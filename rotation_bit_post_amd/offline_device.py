@@ -1,19 +1,25 @@
-"""Offline conversion of a correction site on the device (torch, float64).
+"""Offline conversion of a correction site with its large products on the device (torch, float64).
 
 The same conversion as ``offline.convert_site`` - T = R_out^T R_in, the top-r
 singular subspace of dT = T - I, M = U_r^T T U_r - I_r (ReSpinQuant zh 2.1-2.2;
-it 2C; nl 2B-2C; fr 2B-2C) - run on the GPU so that preparing a model's
-junctions takes a fraction of a second each instead of a host eigensolver's
-tens of seconds at D = 4096.
+it 2C; nl 2B-2C; fr 2B-2C) - with every D x D product on the GPU, so that
+preparing a model's junctions takes about a second each instead of a host
+eigensolver's tens of seconds at D = 4096.
 
 The subspace comes from block subspace iteration on the symmetric positive
 semi-definite S = dT^T dT = 2I - T - T^T (its top-r eigenvectors are dT's top-r
 left and right singular vectors, dT being normal): a block of p = 2r + 8
 vectors is multiplied by S and re-orthonormalised (Cholesky QR) until the
 Rayleigh-Ritz residual of the top r vectors falls below the tolerance. The
-iteration converges at the rate lambda_{p+1} / lambda_r per step. As on the
-host, a rank that splits a pair of equal singular values (no gap at r) is
-refused.
+iteration converges at the rate lambda_{p+1} / lambda_r per step; a site that
+has not converged after max_iters steps is refused, as is a rank that splits a
+pair of equal singular values (no gap at r).
+
+Only matrix products run on the device. The Cayley transform of each rotation
+is a float64 solve on the host (the same routine as the host conversion), and
+the p x p factorisations of the iteration (Cholesky, triangular inverse,
+symmetric eigensolver) run on the host in numpy: they are tiny, and the
+device keeps no dense-solver call.
 """
 from __future__ import annotations
 
@@ -21,27 +27,29 @@ import numpy as np
 
 
 def synthetic_rotation_device(a, eps: float, device="cuda"):
-    """H C(eps A) on the device in float64 (H the normalised Sylvester-Hadamard matrix)."""
+    """H C(eps A) in float64 on the device: the Cayley transform solved on the host, the product with the
+    normalised Sylvester-Hadamard matrix H on the device."""
     import torch
-    from .offline import sylvester_hadamard
-    a = torch.as_tensor(np.asarray(a), dtype=torch.float64, device=device)
-    eye = torch.eye(a.shape[0], dtype=torch.float64, device=device)
-    c = torch.linalg.solve(eye - eps * a, eye + eps * a)
+    from .offline import cayley_rotation, sylvester_hadamard
+    a = np.asarray(a, np.float64)
+    c = torch.as_tensor(cayley_rotation(a, eps), dtype=torch.float64, device=device)
     h = torch.as_tensor(sylvester_hadamard(a.shape[0]), dtype=torch.float64, device=device)
     return h @ c
 
 
 def _cholesky_qr(y):
+    """Orthonormal columns spanning y: y L^-T with L L^T = y^T y (Gram on the device, factor on the host)."""
     import torch
-    g = y.T @ y
-    l = torch.linalg.cholesky(g)
-    return torch.linalg.solve_triangular(l, y.T, upper=False).T  # y L^-T
+    g = (y.T @ y).cpu().numpy()
+    l_inv_t = np.linalg.inv(np.linalg.cholesky(0.5 * (g + g.T))).T
+    return y @ torch.as_tensor(l_inv_t, dtype=y.dtype, device=y.device)
 
 
 def convert_site_device(r_in, r_out, r: int, tol: float = 1e-10, max_iters: int = 3000, seed: int = 0):
     """(U_r, M) in float32 numpy, plus the iteration count and final residual.
 
     r_in, r_out: float64 rotations (torch tensors on the device, or numpy).
+    Raises ValueError if the residual is still >= tol after max_iters steps.
     """
     import torch
     dev = r_in.device if isinstance(r_in, torch.Tensor) else torch.device("cuda")
@@ -60,17 +68,23 @@ def convert_site_device(r_in, r_out, r: int, tol: float = 1e-10, max_iters: int 
     it = 0
     lam = vec = None
     while it < max_iters:
-        for _ in range(10):
+        for _ in range(min(10, max_iters - it)):
             q = _cholesky_qr(s @ q)
-        it += 10
-        # Rayleigh-Ritz on the block
-        h = q.T @ (s @ q)
-        lam, w = torch.linalg.eigh(0.5 * (h + h.T))
-        lam, w = lam.flip(0), w.flip(1)             # descending
-        vec = q @ w[:, :r]
-        res = float(torch.linalg.matrix_norm(s @ vec - vec * lam[:r]) / max(float(lam[0]), 1e-300))
+            it += 1
+        # Rayleigh-Ritz on the block (p x p eigenproblem on the host)
+        sq = s @ q
+        h = (q.T @ sq).cpu().numpy()
+        lam_h, w_h = np.linalg.eigh(0.5 * (h + h.T))
+        lam_h, w_h = lam_h[::-1].copy(), w_h[:, ::-1].copy()      # descending
+        w = torch.as_tensor(w_h[:, :r], dtype=torch.float64, device=dev)
+        vec = q @ w
+        lam = lam_h
+        resid = sq @ w - vec * torch.as_tensor(lam[:r], dtype=torch.float64, device=dev)
+        res = float(torch.linalg.vector_norm(resid) / max(float(lam[0]), 1e-300))
         if res < tol:
             break
+    if not res < tol:
+        raise ValueError(f"subspace iteration did not converge: residual {res:.3e} >= {tol:.1e} after {it} steps")
     if r < d and not float(lam[r - 1] - lam[r]) > 1e-6 * float(lam[0]):
         raise ValueError(f"no singular-value gap at rank {r}")
     m = vec.T @ t @ vec - torch.eye(r, dtype=torch.float64, device=dev)

@@ -214,6 +214,10 @@ class LayerPath:
         for which in self.sites:
             self.bufs[f"codes_{which}"] = torch.empty((n, B.rsq_packed_row_bytes(cfg.D, bits)), dtype=torch.uint8, device="cuda")
             self.bufs[f"scales_{which}"] = torch.empty(n, dtype=torch.float32, device="cuda")
+        # one workspace for every stage (they run one after another on one stream)
+        need = [B.rsq_correct_workspace_bytes(n, cfg.D)]
+        need += [B.rsq_qgemm_workspace_bytes(n, lin.N, lin.K, bits) for lin in self.linears.values()]
+        self.bufs["workspace"] = B.rsq_workspace(max(need))
         for name, lin in self.linears.items():
             self.bufs[f"y_{name}"] = torch.empty((n, lin.N), dtype=ydt, device="cuda")
             if lin.source in ("o_in", "down_in"):
@@ -233,6 +237,7 @@ class LayerPath:
         and the o / down outputs are separate tensors.
         """
         cfg, bits, b = self.cfg, self.code_bits, self.bufs
+        ws = b["workspace"]
         if chain and "B" not in self.sites:
             raise ValueError("a chained layer needs both sites")
         out = []
@@ -244,7 +249,8 @@ class LayerPath:
             codes, scales = b[f"codes_{which}"], b[f"scales_{which}"]
             if correction:
                 fn = (lambda h_in=h_in, h_out=h_out, site=site, codes=codes, scales=scales:
-                      B.rsq_correct_quant(h_in, h_out, site.buf, site.r, codes, scales, bits, eps=self.eps))
+                      B.rsq_correct_quant(h_in, h_out, site.buf, site.r, codes, scales, bits, eps=self.eps,
+                                          workspace=ws))
             else:
                 fn = (lambda h_in=h_in, codes=codes, scales=scales:
                       B.rsq_quant_act(h_in, codes, scales, bits, rmsnorm=True, eps=self.eps))
@@ -270,16 +276,17 @@ class LayerPath:
 
     def _gemm(self, lin: QLinear, codes, scales, residual=None, dst=None):
         """The stage of one linear; with a residual the result goes to dst (added in the epilogue)."""
-        n, bits = self.n, self.cfg.bits
+        n, bits, ws = self.n, self.cfg.bits, self.bufs["workspace"]
         name = f"gemm_{lin.name}" + ("_res" if residual is not None else "")
         y = dst if residual is not None else self.bufs[f"y_{lin.name}"]
         if self.fp4:
             return (name, "gemm", lambda: B.rsq_qgemm_fp4(codes, scales, n, lin.fp4, lin.scales, lin.N, lin.K, y,
-                                                         residual=residual))
+                                                         residual=residual, workspace=ws))
         if residual is not None:
             return (name, "gemm", lambda: B.rsq_qgemm_residual(codes, scales, n, lin.codes, lin.scales, lin.N, lin.K,
-                                                                bits, residual, y))
-        return (name, "gemm", lambda: B.rsq_qgemm(codes, scales, n, lin.codes, lin.scales, lin.N, lin.K, bits, y))
+                                                                bits, residual, y, workspace=ws))
+        return (name, "gemm", lambda: B.rsq_qgemm(codes, scales, n, lin.codes, lin.scales, lin.N, lin.K, bits, y,
+                                                   workspace=ws))
 
     def step(self, correction: bool = True, chain: bool = False):
         for _, _, fn in self.stages(correction, chain):

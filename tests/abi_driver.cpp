@@ -15,6 +15,8 @@ hipError_t g_ret = hipSuccess;
 const void *g_res = nullptr;
 int64_t g_ld_r = -1;
 int g_bits = -1;
+void *g_ws = nullptr;
+size_t g_need_c = 0, g_need_g = 0;
 int g_fail = 0, g_cases = 0;
 
 void expect(const char *what, int got, int want, int launches) {
@@ -36,18 +38,23 @@ hipError_t launch_site_prepare(const float *, const float *, int, int, void *, h
     return g_ret;
 }
 hipError_t launch_correct(const void *, void *, int, int64_t, int, int64_t, const void *, int, bool, const float *,
-                          float, int, uint8_t *, float *, hipStream_t) {
+                          float, int, uint8_t *, float *, void *ws, hipStream_t) {
     ++g_launches;
+    g_ws = ws;
     return g_ret;
 }
+size_t correct_workspace_bytes(int64_t, int64_t) { return g_need_c; }
+size_t qgemm_workspace_bytes(int64_t, int64_t, int64_t, int) { return g_need_g; }
 hipError_t launch_quant(const void *, int, int64_t, int, int64_t, bool, const float *, float, int, uint8_t *, float *,
                         hipStream_t) {
     ++g_launches;
     return g_ret;
 }
 hipError_t launch_qgemm(const uint8_t *, const float *, int64_t, const uint8_t *, const float *, int64_t, int64_t,
-                        int bits, void *, int, int64_t, int32_t *, const void *res, int64_t ld_r, hipStream_t) {
+                        int bits, void *, int, int64_t, int32_t *, const void *res, int64_t ld_r, void *ws,
+                        hipStream_t) {
     ++g_launches;
+    g_ws = ws;
     g_res = res;
     g_ld_r = ld_r;
     g_bits = bits;
@@ -106,25 +113,25 @@ int main() {
     expect("quant misaligned codes", rsq_quant_act(p, RSQ_BF16, 4, 256, 256, 0, nullptr, 0.0f, 4, q + 2, fo, nullptr), RSQ_ERR_INVALID_ARG, 0);
 
     // fused correction + quantisation, and one site with its linear
-    expect("correct_quant ok", rsq_correct_quant(p, q, RSQ_BF16, 4, 256, p, 8, nullptr, 1e-5f, 3, q + 4096, fo + 4096, nullptr), RSQ_OK, 1);
-    expect("correct_quant eps", rsq_correct_quant(p, q, RSQ_BF16, 4, 256, p, 8, nullptr, -1.0f, 3, q + 4096, fo + 4096, nullptr), RSQ_ERR_INVALID_ARG, 0);
-    expect("layer_fused ok", rsq_layer_fused(p, q, RSQ_BF16, 4, 256, p, 8, nullptr, 1e-5f, 4, q + 4096, fo + 4096, p, f, 64, q + 8192, RSQ_BF16, nullptr), RSQ_OK, 2);
-    expect("layer_fused n_out", rsq_layer_fused(p, q, RSQ_BF16, 4, 256, p, 8, nullptr, 1e-5f, 4, q + 4096, fo + 4096, p, f, 48, q + 8192, RSQ_BF16, nullptr), RSQ_ERR_INVALID_ARG, 0);
+    expect("correct_quant ok", rsq_correct_quant(p, q, RSQ_BF16, 4, 256, p, 8, nullptr, 1e-5f, 3, q + 4096, fo + 4096, nullptr, 0, nullptr), RSQ_OK, 1);
+    expect("correct_quant eps", rsq_correct_quant(p, q, RSQ_BF16, 4, 256, p, 8, nullptr, -1.0f, 3, q + 4096, fo + 4096, nullptr, 0, nullptr), RSQ_ERR_INVALID_ARG, 0);
+    expect("layer_fused ok", rsq_layer_fused(p, q, RSQ_BF16, 4, 256, p, 8, nullptr, 1e-5f, 4, q + 4096, fo + 4096, p, f, 64, q + 8192, RSQ_BF16, nullptr, 0, nullptr), RSQ_OK, 2);
+    expect("layer_fused n_out", rsq_layer_fused(p, q, RSQ_BF16, 4, 256, p, 8, nullptr, 1e-5f, 4, q + 4096, fo + 4096, p, f, 48, q + 8192, RSQ_BF16, nullptr, 0, nullptr), RSQ_ERR_INVALID_ARG, 0);
 
     // GEMMs
-    expect("qgemm ok", rsq_qgemm(p, f, 4, p, f, 64, 128, 4, q, RSQ_BF16, 64, nullptr, nullptr), RSQ_OK, 1);
-    expect("qgemm n = 0", rsq_qgemm(nullptr, nullptr, 0, nullptr, nullptr, 64, 128, 4, nullptr, RSQ_BF16, 64, nullptr, nullptr), RSQ_OK, 0);
-    expect("qgemm bits", rsq_qgemm(p, f, 4, p, f, 64, 128, 2, q, RSQ_BF16, 64, nullptr, nullptr), RSQ_ERR_INVALID_ARG, 0);
-    expect("qgemm n_out", rsq_qgemm(p, f, 4, p, f, 40, 128, 4, q, RSQ_BF16, 64, nullptr, nullptr), RSQ_ERR_INVALID_ARG, 0);
-    expect("qgemm k max", rsq_qgemm(p, f, 4, p, f, 64, 65568, 4, q, RSQ_BF16, 64, nullptr, nullptr), RSQ_ERR_UNSUPPORTED, 0);
-    expect("qgemm ld_y", rsq_qgemm(p, f, 4, p, f, 64, 128, 4, q, RSQ_BF16, 32, nullptr, nullptr), RSQ_ERR_INVALID_ARG, 0);
-    expect("qgemm acc misaligned", rsq_qgemm(p, f, 4, p, f, 64, 128, 4, q, RSQ_BF16, 64, reinterpret_cast<int32_t *>(q + 4), nullptr), RSQ_ERR_INVALID_ARG, 0);
-    expect("residual ok", rsq_qgemm_residual(p, f, 4, p, f, 64, 128, 4, q, 64, q + 65536, RSQ_BF16, 64, nullptr), RSQ_OK, 1);
+    expect("qgemm ok", rsq_qgemm(p, f, 4, p, f, 64, 128, 4, q, RSQ_BF16, 64, nullptr, nullptr, 0, nullptr), RSQ_OK, 1);
+    expect("qgemm n = 0", rsq_qgemm(nullptr, nullptr, 0, nullptr, nullptr, 64, 128, 4, nullptr, RSQ_BF16, 64, nullptr, nullptr, 0, nullptr), RSQ_OK, 0);
+    expect("qgemm bits", rsq_qgemm(p, f, 4, p, f, 64, 128, 2, q, RSQ_BF16, 64, nullptr, nullptr, 0, nullptr), RSQ_ERR_INVALID_ARG, 0);
+    expect("qgemm n_out", rsq_qgemm(p, f, 4, p, f, 40, 128, 4, q, RSQ_BF16, 64, nullptr, nullptr, 0, nullptr), RSQ_ERR_INVALID_ARG, 0);
+    expect("qgemm k max", rsq_qgemm(p, f, 4, p, f, 64, 65568, 4, q, RSQ_BF16, 64, nullptr, nullptr, 0, nullptr), RSQ_ERR_UNSUPPORTED, 0);
+    expect("qgemm ld_y", rsq_qgemm(p, f, 4, p, f, 64, 128, 4, q, RSQ_BF16, 32, nullptr, nullptr, 0, nullptr), RSQ_ERR_INVALID_ARG, 0);
+    expect("qgemm acc misaligned", rsq_qgemm(p, f, 4, p, f, 64, 128, 4, q, RSQ_BF16, 64, reinterpret_cast<int32_t *>(q + 4), nullptr, 0, nullptr), RSQ_ERR_INVALID_ARG, 0);
+    expect("residual ok", rsq_qgemm_residual(p, f, 4, p, f, 64, 128, 4, q, 64, q + 65536, RSQ_BF16, 64, nullptr, 0, nullptr), RSQ_OK, 1);
     if (g_res != q || g_ld_r != 64) { std::printf("FAIL residual not passed to the launcher\n"); ++g_fail; }
-    expect("residual in place", rsq_qgemm_residual(p, f, 4, p, f, 64, 128, 4, q, 64, q, RSQ_BF16, 64, nullptr), RSQ_OK, 1);
-    expect("residual in place ld", rsq_qgemm_residual(p, f, 4, p, f, 64, 128, 4, q, 96, q, RSQ_BF16, 64, nullptr), RSQ_ERR_INVALID_ARG, 0);
-    expect("residual overlap", rsq_qgemm_residual(p, f, 4, p, f, 64, 128, 4, q, 64, q + 64, RSQ_BF16, 64, nullptr), RSQ_ERR_INVALID_ARG, 0);
-    expect("residual null", rsq_qgemm_residual(p, f, 4, p, f, 64, 128, 4, nullptr, 64, q, RSQ_BF16, 64, nullptr), RSQ_ERR_INVALID_ARG, 0);
+    expect("residual in place", rsq_qgemm_residual(p, f, 4, p, f, 64, 128, 4, q, 64, q, RSQ_BF16, 64, nullptr, 0, nullptr), RSQ_OK, 1);
+    expect("residual in place ld", rsq_qgemm_residual(p, f, 4, p, f, 64, 128, 4, q, 96, q, RSQ_BF16, 64, nullptr, 0, nullptr), RSQ_ERR_INVALID_ARG, 0);
+    expect("residual overlap", rsq_qgemm_residual(p, f, 4, p, f, 64, 128, 4, q, 64, q + 64, RSQ_BF16, 64, nullptr, 0, nullptr), RSQ_ERR_INVALID_ARG, 0);
+    expect("residual null", rsq_qgemm_residual(p, f, 4, p, f, 64, 128, 4, nullptr, 64, q, RSQ_BF16, 64, nullptr, 0, nullptr), RSQ_ERR_INVALID_ARG, 0);
 
     // fp4 codes: conversion and the linear on them
     expect("to_fp4 ok", rsq_codes_to_fp4(p, 4, 256, q, nullptr), RSQ_OK, 1);
@@ -134,32 +141,63 @@ int main() {
     expect("to_fp4 overlap", rsq_codes_to_fp4(p, 4, 256, p + 256, nullptr), RSQ_ERR_INVALID_ARG, 0);
     expect("to_fp4 misaligned", rsq_codes_to_fp4(p, 4, 256, q + 8, nullptr), RSQ_ERR_INVALID_ARG, 0);
     expect("to_fp4 null", rsq_codes_to_fp4(p, 4, 256, nullptr, nullptr), RSQ_ERR_INVALID_ARG, 0);
-    expect("fp4 qgemm ok", rsq_qgemm_fp4(p, f, 4, p, f, 64, 128, nullptr, 0, q, RSQ_BF16, 64, nullptr, nullptr), RSQ_OK, 1);
+    expect("fp4 qgemm ok", rsq_qgemm_fp4(p, f, 4, p, f, 64, 128, nullptr, 0, q, RSQ_BF16, 64, nullptr, nullptr, 0, nullptr), RSQ_OK, 1);
     if (g_bits != rsq::kFp4 || g_res != nullptr) { std::printf("FAIL fp4 qgemm: wrong code format or residual at the launcher\n"); ++g_fail; }
-    expect("fp4 qgemm residual", rsq_qgemm_fp4(p, f, 4, p, f, 64, 128, q + 65536, 64, q, RSQ_BF16, 64, nullptr, nullptr), RSQ_OK, 1);
+    expect("fp4 qgemm residual", rsq_qgemm_fp4(p, f, 4, p, f, 64, 128, q + 65536, 64, q, RSQ_BF16, 64, nullptr, nullptr, 0, nullptr), RSQ_OK, 1);
     if (g_res != q + 65536 || g_ld_r != 64) { std::printf("FAIL fp4 qgemm: residual not passed to the launcher\n"); ++g_fail; }
-    expect("fp4 qgemm in place", rsq_qgemm_fp4(p, f, 4, p, f, 64, 128, q, 64, q, RSQ_F32, 64, nullptr, nullptr), RSQ_OK, 1);
-    expect("fp4 qgemm in place ld", rsq_qgemm_fp4(p, f, 4, p, f, 64, 128, q, 96, q, RSQ_F32, 64, nullptr, nullptr), RSQ_ERR_INVALID_ARG, 0);
-    expect("fp4 qgemm overlap", rsq_qgemm_fp4(p, f, 4, p, f, 64, 128, q + 64, 64, q, RSQ_BF16, 64, nullptr, nullptr), RSQ_ERR_INVALID_ARG, 0);
-    expect("fp4 qgemm k max", rsq_qgemm_fp4(p, f, 4, p, f, 64, 65568, nullptr, 0, q, RSQ_BF16, 64, nullptr, nullptr), RSQ_ERR_UNSUPPORTED, 0);
-    expect("fp4 qgemm n = 0", rsq_qgemm_fp4(nullptr, nullptr, 0, nullptr, nullptr, 64, 128, nullptr, 0, nullptr, RSQ_BF16, 64, nullptr, nullptr), RSQ_OK, 0);
-    expect("fp4 qgemm acc misaligned", rsq_qgemm_fp4(p, f, 4, p, f, 64, 128, nullptr, 0, q, RSQ_BF16, 64, reinterpret_cast<int32_t *>(q + 4), nullptr), RSQ_ERR_INVALID_ARG, 0);
-    expect("qgemm int3 format", rsq_qgemm(p, f, 4, p, f, 64, 128, 3, q, RSQ_BF16, 64, nullptr, nullptr), RSQ_OK, 1);
+    expect("fp4 qgemm in place", rsq_qgemm_fp4(p, f, 4, p, f, 64, 128, q, 64, q, RSQ_F32, 64, nullptr, nullptr, 0, nullptr), RSQ_OK, 1);
+    expect("fp4 qgemm in place ld", rsq_qgemm_fp4(p, f, 4, p, f, 64, 128, q, 96, q, RSQ_F32, 64, nullptr, nullptr, 0, nullptr), RSQ_ERR_INVALID_ARG, 0);
+    expect("fp4 qgemm overlap", rsq_qgemm_fp4(p, f, 4, p, f, 64, 128, q + 64, 64, q, RSQ_BF16, 64, nullptr, nullptr, 0, nullptr), RSQ_ERR_INVALID_ARG, 0);
+    expect("fp4 qgemm k max", rsq_qgemm_fp4(p, f, 4, p, f, 64, 65568, nullptr, 0, q, RSQ_BF16, 64, nullptr, nullptr, 0, nullptr), RSQ_ERR_UNSUPPORTED, 0);
+    expect("fp4 qgemm n = 0", rsq_qgemm_fp4(nullptr, nullptr, 0, nullptr, nullptr, 64, 128, nullptr, 0, nullptr, RSQ_BF16, 64, nullptr, nullptr, 0, nullptr), RSQ_OK, 0);
+    expect("fp4 qgemm acc misaligned", rsq_qgemm_fp4(p, f, 4, p, f, 64, 128, nullptr, 0, q, RSQ_BF16, 64, reinterpret_cast<int32_t *>(q + 4), nullptr, 0, nullptr), RSQ_ERR_INVALID_ARG, 0);
+    expect("qgemm int3 format", rsq_qgemm(p, f, 4, p, f, 64, 128, 3, q, RSQ_BF16, 64, nullptr, nullptr, 0, nullptr), RSQ_OK, 1);
     if (g_bits != 3) { std::printf("FAIL int3 qgemm: wrong code format at the launcher\n"); ++g_fail; }
-    expect("qgemm fp4 bits", rsq_qgemm(p, f, 4, p, f, 64, 128, 3 | RSQ_FP4, q, RSQ_BF16, 64, nullptr, nullptr), RSQ_OK, 1);
+    expect("qgemm fp4 bits", rsq_qgemm(p, f, 4, p, f, 64, 128, 3 | RSQ_FP4, q, RSQ_BF16, 64, nullptr, nullptr, 0, nullptr), RSQ_OK, 1);
     if (g_bits != rsq::kFp4) { std::printf("FAIL qgemm bits 3 | RSQ_FP4: wrong code format at the launcher\n"); ++g_fail; }
-    expect("qgemm 4 | RSQ_FP4", rsq_qgemm(p, f, 4, p, f, 64, 128, 4 | RSQ_FP4, q, RSQ_BF16, 64, nullptr, nullptr), RSQ_ERR_INVALID_ARG, 0);
+    expect("qgemm 4 | RSQ_FP4", rsq_qgemm(p, f, 4, p, f, 64, 128, 4 | RSQ_FP4, q, RSQ_BF16, 64, nullptr, nullptr, 0, nullptr), RSQ_ERR_INVALID_ARG, 0);
     expect("quant fp4 codes", rsq_quant_act(p, RSQ_BF16, 4, 256, 256, RSQ_QA_RMSNORM, nullptr, 1e-5f, 3 | RSQ_FP4, q, fo, nullptr), RSQ_OK, 1);
-    expect("correct_quant fp4 codes", rsq_correct_quant(p, q, RSQ_BF16, 4, 256, p, 8, nullptr, 1e-5f, 3 | RSQ_FP4, q + 4096, fo + 4096, nullptr), RSQ_OK, 1);
-    expect("layer_fused fp4", rsq_layer_fused(p, q, RSQ_BF16, 4, 256, p, 8, nullptr, 1e-5f, 3 | RSQ_FP4, q + 4096, fo + 4096, p, f, 64, q + 8192, RSQ_BF16, nullptr), RSQ_OK, 2);
+    expect("correct_quant fp4 codes", rsq_correct_quant(p, q, RSQ_BF16, 4, 256, p, 8, nullptr, 1e-5f, 3 | RSQ_FP4, q + 4096, fo + 4096, nullptr, 0, nullptr), RSQ_OK, 1);
+    expect("layer_fused fp4", rsq_layer_fused(p, q, RSQ_BF16, 4, 256, p, 8, nullptr, 1e-5f, 3 | RSQ_FP4, q + 4096, fo + 4096, p, f, 64, q + 8192, RSQ_BF16, nullptr, 0, nullptr), RSQ_OK, 2);
     if (g_bits != rsq::kFp4) { std::printf("FAIL layer_fused bits 3 | RSQ_FP4: wrong code format at the GEMM\n"); ++g_fail; }
     expect("row bytes fp4", rsq_packed_row_bytes(64, 3 | RSQ_FP4) == 32 ? 0 : 1, 0, 0);
 
+    // workspace: sized by the queries, checked before any launch, passed to the launchers
+    g_need_g = 4096;
+    expect("query qgemm ws", rsq_qgemm_workspace_bytes(4, 64, 128, 4) == 4096 ? 0 : 1, 0, 0);
+    expect("query qgemm ws bad k", rsq_qgemm_workspace_bytes(4, 64, 100, 4) == 0 ? 0 : 1, 0, 0);
+    expect("query qgemm ws bad bits", rsq_qgemm_workspace_bytes(4, 64, 128, 5) == 0 ? 0 : 1, 0, 0);
+    expect("qgemm ws missing", rsq_qgemm(p, f, 4, p, f, 64, 128, 4, q, RSQ_BF16, 64, nullptr, nullptr, 0, nullptr), RSQ_ERR_WORKSPACE, 0);
+    expect("qgemm ws small", rsq_qgemm(p, f, 4, p, f, 64, 128, 4, q, RSQ_BF16, 64, nullptr, q + 65536, 4095, nullptr), RSQ_ERR_WORKSPACE, 0);
+    expect("qgemm ws misaligned", rsq_qgemm(p, f, 4, p, f, 64, 128, 4, q, RSQ_BF16, 64, nullptr, q + 65540, 8192, nullptr), RSQ_ERR_WORKSPACE, 0);
+    expect("qgemm ws ok", rsq_qgemm(p, f, 4, p, f, 64, 128, 4, q, RSQ_BF16, 64, nullptr, q + 65536, 4096, nullptr), RSQ_OK, 1);
+    if (g_ws != q + 65536) { std::printf("FAIL qgemm: workspace not passed to the launcher\n"); ++g_fail; }
+    expect("residual ws missing", rsq_qgemm_residual(p, f, 4, p, f, 64, 128, 4, q, 64, q, RSQ_BF16, 64, nullptr, 0, nullptr), RSQ_ERR_WORKSPACE, 0);
+    expect("fp4 qgemm ws missing", rsq_qgemm_fp4(p, f, 4, p, f, 64, 128, nullptr, 0, q, RSQ_BF16, 64, nullptr, nullptr, 0, nullptr), RSQ_ERR_WORKSPACE, 0);
+    g_need_g = 0;
+    g_need_c = 1024;
+    expect("query correct ws", rsq_correct_workspace_bytes(4, 256) == 1024 ? 0 : 1, 0, 0);
+    expect("query correct ws bad d", rsq_correct_workspace_bytes(4, 250) == 0 ? 0 : 1, 0, 0);
+    expect("correct_quant ws missing", rsq_correct_quant(p, q, RSQ_BF16, 4, 256, p, 8, nullptr, 1e-5f, 4, q + 4096, fo + 4096, nullptr, 0, nullptr), RSQ_ERR_WORKSPACE, 0);
+    expect("correct_quant ws ok", rsq_correct_quant(p, q, RSQ_BF16, 4, 256, p, 8, nullptr, 1e-5f, 4, q + 4096, fo + 4096, q + 65536, 1024, nullptr), RSQ_OK, 1);
+    if (g_ws != q + 65536) { std::printf("FAIL correct_quant: workspace not passed to the launcher\n"); ++g_fail; }
+    expect("correction alone needs none", rsq_subspace_correct(p, q, RSQ_BF16, 4, 256, 256, p, 8, nullptr), RSQ_OK, 1);
+    g_need_g = 2048;
+    expect("query layer ws", rsq_layer_workspace_bytes(4, 256, 64, 4) == 2048 ? 0 : 1, 0, 0);
+    expect("layer_fused ws small", rsq_layer_fused(p, q, RSQ_BF16, 4, 256, p, 8, nullptr, 1e-5f, 4, q + 4096, fo + 4096, p, f, 64, q + 8192, RSQ_BF16, q + 65536, 1024, nullptr), RSQ_ERR_WORKSPACE, 0);
+    expect("layer_fused ws ok", rsq_layer_fused(p, q, RSQ_BF16, 4, 256, p, 8, nullptr, 1e-5f, 4, q + 4096, fo + 4096, p, f, 64, q + 8192, RSQ_BF16, q + 65536, 2048, nullptr), RSQ_OK, 2);
+    g_need_c = g_need_g = 0;
+    // norm weights are read with 16-byte loads
+    expect("quant norm_w misaligned", rsq_quant_act(p, RSQ_BF16, 4, 256, 256, RSQ_QA_RMSNORM, f + 1, 1e-5f, 4, q, fo, nullptr), RSQ_ERR_INVALID_ARG, 0);
+    expect("correct_quant norm_w misaligned", rsq_correct_quant(p, q, RSQ_BF16, 4, 256, p, 8, f + 2, 1e-5f, 4, q + 4096, fo + 4096, nullptr, 0, nullptr), RSQ_ERR_INVALID_ARG, 0);
+    expect("layer_fused norm_w misaligned", rsq_layer_fused(p, q, RSQ_BF16, 4, 256, p, 8, f + 3, 1e-5f, 4, q + 4096, fo + 4096, p, f, 64, q + 8192, RSQ_BF16, nullptr, 0, nullptr), RSQ_ERR_INVALID_ARG, 0);
+    expect("quant norm_w aligned", rsq_quant_act(p, RSQ_BF16, 4, 256, 256, RSQ_QA_RMSNORM, f + 4, 1e-5f, 4, q, fo, nullptr), RSQ_OK, 1);
+
     // a launch failure surfaces as RSQ_ERR_HIP with a message; the fused call stops after the failed launch
     g_ret = hipErrorInvalidValue;
-    expect("launch failure", rsq_qgemm(p, f, 4, p, f, 64, 128, 4, q, RSQ_BF16, 64, nullptr, nullptr), RSQ_ERR_HIP, 1);
+    expect("launch failure", rsq_qgemm(p, f, 4, p, f, 64, 128, 4, q, RSQ_BF16, 64, nullptr, nullptr, 0, nullptr), RSQ_ERR_HIP, 1);
     expect("launch failure to_fp4", rsq_codes_to_fp4(p, 4, 256, q, nullptr), RSQ_ERR_HIP, 1);
-    expect("launch failure fused", rsq_layer_fused(p, q, RSQ_BF16, 4, 256, p, 8, nullptr, 1e-5f, 4, q + 4096, fo + 4096, p, f, 64, q + 8192, RSQ_BF16, nullptr), RSQ_ERR_HIP, 1);
+    expect("launch failure fused", rsq_layer_fused(p, q, RSQ_BF16, 4, 256, p, 8, nullptr, 1e-5f, 4, q + 4096, fo + 4096, p, f, 64, q + 8192, RSQ_BF16, nullptr, 0, nullptr), RSQ_ERR_HIP, 1);
     g_ret = hipSuccess;
 
     std::printf("%s: %d cases, %d failed\n", g_fail ? "FAILED" : "ok", g_cases, g_fail);

@@ -89,6 +89,7 @@ def test_subspace_correct_validation(args, status, needle):
     ((FAKE, 1, 4, 4096, 4096, 1, None, -1.0, 4, FAKE, FAKE, None), 1, "eps"),
     ((FAKE, 1, 4, 4096, 4096, 0, None, 1e-5, 4, None, FAKE, None), 1, "null pointer"),
     ((None, 1, 4, 4096, 4096, 0, None, 1e-5, 4, FAKE, FAKE, None), 1, "x must be"),
+    ((FAKE, 1, 4, 4096, 4096, 1, FAKE + 8, 1e-5, 4, FAKE, FAKE, None), 1, "norm_w"),
 ])
 def test_quant_act_validation(args, status, needle):
     st, msg = _call("rsq_quant_act", *args)
@@ -96,13 +97,13 @@ def test_quant_act_validation(args, status, needle):
 
 
 @pytest.mark.parametrize("args,status,needle", [
-    ((FAKE, FAKE, 8, FAKE, FAKE, 100, 4096, 4, FAKE, 1, 100, None, None), 1, "n_out"),
-    ((FAKE, FAKE, 8, FAKE, FAKE, 128, 4016, 4, FAKE, 1, 128, None, None), 1, "multiple of 32"),
-    ((FAKE, FAKE, 8, FAKE, FAKE, 128, 4096, 2, FAKE, 1, 128, None, None), 1, "bits"),
-    ((FAKE, FAKE, 8, FAKE, FAKE, 128, 4096, 4, FAKE, 1, 64, None, None), 1, "ld_y"),
-    ((FAKE, FAKE, 8, FAKE, FAKE, 128, 131072, 4, FAKE, 1, 128, None, None), 2, "65536"),
-    ((FAKE, FAKE, 8, None, FAKE, 128, 4096, 4, FAKE, 1, 128, None, None), 1, "null pointer"),
-    ((FAKE, FAKE, 8, FAKE, FAKE, 128, 4096, 4, FAKE, 1, 128, FAKE + 4, None), 1, "acc_out"),
+    ((FAKE, FAKE, 8, FAKE, FAKE, 100, 4096, 4, FAKE, 1, 100, None, None, 0, None), 1, "n_out"),
+    ((FAKE, FAKE, 8, FAKE, FAKE, 128, 4016, 4, FAKE, 1, 128, None, None, 0, None), 1, "multiple of 32"),
+    ((FAKE, FAKE, 8, FAKE, FAKE, 128, 4096, 2, FAKE, 1, 128, None, None, 0, None), 1, "bits"),
+    ((FAKE, FAKE, 8, FAKE, FAKE, 128, 4096, 4, FAKE, 1, 64, None, None, 0, None), 1, "ld_y"),
+    ((FAKE, FAKE, 8, FAKE, FAKE, 128, 131072, 4, FAKE, 1, 128, None, None, 0, None), 2, "65536"),
+    ((FAKE, FAKE, 8, None, FAKE, 128, 4096, 4, FAKE, 1, 128, None, None, 0, None), 1, "null pointer"),
+    ((FAKE, FAKE, 8, FAKE, FAKE, 128, 4096, 4, FAKE, 1, 128, FAKE + 4, None, 0, None), 1, "acc_out"),
 ])
 def test_qgemm_validation(args, status, needle):
     st, msg = _call("rsq_qgemm", *args)
@@ -111,28 +112,37 @@ def test_qgemm_validation(args, status, needle):
 
 def test_qgemm_residual_validation():
     # (a, sa, n, w, sw, n_out, k, bits, residual, ld_r, y, y_dtype, ld_y, stream)
-    st, msg = _call("rsq_qgemm_residual", FAKE, FAKE, 4, FAKE, FAKE, 128, 256, 4, None, 128, FAKE, 1, 128, None)
+    # (a, sa, n, w, sw, n_out, k, bits, residual, ld_r, y, y_dtype, ld_y, workspace, workspace_bytes, stream)
+    st, msg = _call("rsq_qgemm_residual", FAKE, FAKE, 4, FAKE, FAKE, 128, 256, 4, None, 128, FAKE, 1, 128, None, 0, None)
     assert st == 1 and "null" in msg
-    st, msg = _call("rsq_qgemm_residual", FAKE, FAKE, 4, FAKE, FAKE, 128, 256, 4, FAKE, 64, FAKE + 4096, 1, 128, None)
+    st, msg = _call("rsq_qgemm_residual", FAKE, FAKE, 4, FAKE, FAKE, 128, 256, 4, FAKE, 64, FAKE + 4096, 1, 128, None, 0,
+                    None)
     assert st == 1 and "ld_r" in msg
-    st, msg = _call("rsq_qgemm_residual", FAKE, FAKE, 4, FAKE, FAKE, 128, 256, 4, FAKE, 128, FAKE + 64, 1, 128, None)
+    st, msg = _call("rsq_qgemm_residual", FAKE, FAKE, 4, FAKE, FAKE, 128, 256, 4, FAKE, 128, FAKE + 64, 1, 128, None, 0,
+                    None)
     assert st == 1 and "overlap" in msg
-    st, msg = _call("rsq_qgemm_residual", FAKE, FAKE, 4, FAKE, FAKE, 128, 256, 4, FAKE, 160, FAKE, 1, 128, None)
+    st, msg = _call("rsq_qgemm_residual", FAKE, FAKE, 4, FAKE, FAKE, 128, 256, 4, FAKE, 160, FAKE, 1, 128, None, 0, None)
     assert st == 1 and "in place" in msg
-    assert _call("rsq_qgemm_residual", None, None, 0, None, None, 128, 256, 4, None, 128, None, 1, 128, None)[0] == 0
+    assert _call("rsq_qgemm_residual", None, None, 0, None, None, 128, 256, 4, None, 128, None, 1, 128, None, 0,
+                 None)[0] == 0
 
 
 def test_empty_batches_are_accepted_without_pointers():
     # n = 0 enqueues nothing, so it needs neither data pointers nor a device
     assert _call("rsq_subspace_correct", None, None, 1, 0, 4096, 4096, None, 32, None)[0] == 0
     assert _call("rsq_quant_act", None, 1, 0, 4096, 4096, 0, None, 1e-5, 4, None, None, None)[0] == 0
-    assert _call("rsq_qgemm", None, None, 0, None, None, 128, 4096, 4, None, 1, 128, None, None)[0] == 0
+    assert _call("rsq_qgemm", None, None, 0, None, None, 128, 4096, 4, None, 1, 128, None, None, 0, None)[0] == 0
+    assert _call("rsq_correct_quant", None, None, 1, 0, 4096, None, 32, None, C.c_float(1e-5), 4, None, None, None, 0,
+                 None)[0] == 0
 
 
 def test_layer_fused_and_site_prepare_validation():
     st, msg = _call("rsq_layer_fused", FAKE, FAKE, 1, 4, 4096, FAKE, 32, None, C.c_float(1e-5), 4, FAKE, FAKE,
-                    FAKE, FAKE, 100, FAKE, 1, None)
+                    FAKE, FAKE, 100, FAKE, 1, None, 0, None)
     assert st == 1 and "n_out" in msg
+    st, msg = _call("rsq_layer_fused", FAKE, FAKE, 1, 4, 4096, FAKE, 32, FAKE + 4, C.c_float(1e-5), 4, FAKE, FAKE,
+                    FAKE, FAKE, 128, FAKE, 1, None, 0, None)
+    assert st == 1 and "norm_w" in msg
     st, msg = _call("rsq_site_prepare", FAKE, FAKE, 4096, 128, FAKE, None)
     assert st == 2 and "exceeds" in msg
     st, msg = _call("rsq_site_prepare", None, FAKE, 4096, 32, FAKE, None)

@@ -543,3 +543,57 @@ def test_many_blocks_norm_weight_and_determinism():
                             quant_input(to_host(h1), True, 1e-5, w), s1.cpu().numpy())[0]
     assert np.all(np.abs(s1.cpu().numpy() - s_ref) <= 1e-6 * s_ref)
 
+
+
+SMALL_SITE_CASES = [  # dtype, d, r, n, bits, weighted: batches small enough for the column-split site
+    ("bf16", 4096, 32, 1, 4, False), ("bf16", 4096, 32, 8, 3, True), ("bf16", 4096, 32, 64, 4, False),
+    ("bf16", 4096, 32, 17, 3 | 0x100, False), ("bf16", 8192, 32, 5, 4, True), ("f32", 1024, 16, 9, 4, False),
+    ("bf16", 2048, 64, 24, 3, False),
+]
+
+
+@pytest.mark.parametrize("dtype,d,r,n,bits,weighted", SMALL_SITE_CASES)
+def test_small_batch_site_matches_oracle_and_the_two_step_form(dtype, d, r, n, bits, weighted):
+    """A few tokens: the column-split correction whose last workgroup per token
+    block quantises the block (one launch, counters in the workspace). h' equals
+    the correction alone bit for bit; codes and scales match the oracle
+    quantiser on the GPU's own h'; a second call on the same workspace (its
+    counters back at zero) repeats the first exactly."""
+    rsq = lib()
+    import torch
+    print(f"case small site dtype={dtype} d={d} r={r} n={n} bits={bits} w={weighted}", flush=True)
+    assert rsq.rsq_correct_workspace_bytes(n, d) > 0
+    U, M = random_site(d, r, seed=d + n) if d <= 2048 else subspace_site(d, r, seed=d + n)
+    site = gpu_site(U, M)
+    h = residual(n, d, dtype, seed=n + 5)
+    w = np.random.default_rng(n).uniform(0.5, 1.5, d).astype(np.float32) if weighted else None
+    wd = None if w is None else to_dev(w, "f32")
+    hd = to_dev(h, dtype)
+    ws = rsq.rsq_workspace(rsq.rsq_correct_workspace_bytes(n, d))
+    rb = rsq.rsq_packed_row_bytes(d, bits)
+    outs = []
+    for _ in range(2):
+        h1, c1, s1 = torch.empty_like(hd), empty_u8(n, rb), empty_f32(n)
+        rsq.rsq_correct_quant(hd, h1, site, r, c1, s1, bits, norm_w=wd, workspace=ws)
+        outs.append((h1, c1, s1))
+    h2 = torch.empty_like(hd)
+    rsq.rsq_subspace_correct(hd, h2, site, r)
+    torch.cuda.synchronize()
+    assert all(torch.equal(a, b) for a, b in zip(outs[0], outs[1]))
+    assert not ws.any()                                   # every counter back at zero
+    h1, c1, s1 = outs[0]
+    assert torch.equal(h1, h2)
+    hp = to_host(h1)
+    err = rel_l2(hp, online.correct(h, U, M, dtype))
+    assert err <= (1e-5 if dtype == "f32" else 2 * bf16_rounding_error(h, U, M))
+    code_bits = 3 if bits != 4 else 4
+    q_ref, s_ref = online.quant_act(hp, code_bits, True, 1e-5, w)
+    if bits == (3 | 0x100):
+        q_gpu = packing.unpack_fp4(c1.cpu().numpy(), d)
+    else:
+        q_gpu = packing.unpack(c1.cpu().numpy(), d, bits)
+    s_gpu = s1.cpu().numpy()
+    ok, nbad, _, nontie = code_mismatch_ok(q_gpu, q_ref, quant_input(hp, True, 1e-5, w), s_gpu)
+    print(f"  rel_l2={err:.2e} tie codes={nbad} not at a tie={nontie}", flush=True)
+    assert ok
+    assert np.all(np.abs(s_gpu - s_ref) <= 1e-6 * s_ref)

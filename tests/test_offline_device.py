@@ -46,3 +46,12 @@ def test_device_conversion_refuses_a_rank_inside_a_pair():
     r_out = synthetic_rotation_device(a_out, cfg.eps_rot, device="cpu")
     with pytest.raises(ValueError):
         convert_site_device(r_in, r_out, 7)
+
+
+def test_device_conversion_refuses_an_unconverged_subspace():
+    cfg = synth.WORKLOADS[synth.TINY]
+    a_in, a_out = synth.skew_generator(cfg, "A", "in"), synth.skew_generator(cfg, "A", "out")
+    r_in = synthetic_rotation_device(a_in, cfg.eps_rot, device="cpu")
+    r_out = synthetic_rotation_device(a_out, cfg.eps_rot, device="cpu")
+    with pytest.raises(ValueError, match="did not converge"):
+        convert_site_device(r_in, r_out, 8, max_iters=3)
