@@ -18,8 +18,12 @@ Inside it a dense r x r transform acts, applied as M = R_sub - I_r
 (zh §2.2 step 2). The pages learn R_sub; here it takes the closed form
 Q_r = U_r^T T U_r, the compression of T onto the subspace.
 
-Weights. Per-output-channel symmetric absmax quantisation with
-round-to-nearest (the pages name only W4/W3; same rule as the activations).
+Weights. The rotations are fused into the weights offline (zh §2.2, offline
+weight fusion, e.g. W~ = R^T W R; fr §2A, W~ = W R): for a row h in a basis
+rotated by R (h~ = h R) a linear y = h W^T equals y = h~ (W R)^T, and an
+output kept in a basis R' is y R' = h~ (R'^T W R)^T. Then per-output-channel
+symmetric absmax quantisation with round-to-nearest (the pages name only
+W4/W3; same rule as the activations).
 """
 from __future__ import annotations
 
@@ -91,6 +95,19 @@ def site(a_in: np.ndarray, a_out: np.ndarray, eps: float, r: int):
     m = subspace_transform(t, u_r)
     return {"T": t, "sigma": sigma, "U": u_r, "M": m,
             "U32": u_r.astype(np.float32), "M32": m.astype(np.float32)}
+
+
+def fuse_weight(w: np.ndarray, right=None, left=None) -> np.ndarray:
+    """W~ = left^T W right in float64 (an absent side is the identity), rounded once to float32.
+
+    right: the rotation of the linear's input basis (K x K); left: the rotation of
+    its output basis (N x N)."""
+    f = np.asarray(w, np.float32).astype(np.float64)
+    if right is not None:
+        f = f @ np.asarray(right, np.float32).astype(np.float64)
+    if left is not None:
+        f = np.asarray(left, np.float32).astype(np.float64).T @ f
+    return f.astype(np.float32)
 
 
 def quantize_weight(w: np.ndarray, bits: int):

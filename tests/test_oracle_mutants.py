@@ -150,3 +150,11 @@ def test_quantising_the_uncorrected_residual_is_caught(monkeypatch):
     monkeypatch.setattr(online, "layer_fused", bad)
     _expect_failure(T_on.test_layer_fused_with_a_quarter_turn_site)
     _expect_failure(T_on.test_layer_linear_path_wires_each_linear_to_its_input)
+
+
+def test_transposed_fusion_rotation_is_caught(monkeypatch):
+    real = prep.fuse_weight
+    monkeypatch.setattr(prep, "fuse_weight",
+                        lambda w, right=None, left=None: real(w, None if right is None else np.asarray(right).T,
+                                                              None if left is None else np.asarray(left).T))
+    _expect_failure(T_pre.test_fused_linear_on_the_rotated_input_is_the_original_linear)

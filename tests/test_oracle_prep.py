@@ -141,3 +141,47 @@ def test_weight_quantisation_is_per_output_channel():
     q, s = prep.quantize_weight(w, 4)
     assert np.allclose(s, np.array([0.7, 2.0], np.float32) / np.float32(7))
     assert q[0, 1] == -7 and q[1, 0] == 7
+
+
+# ---------------------------------------------------------- weight fusion
+def _orth(d, seed):
+    return prep.rotation(_skew(d, seed), 0.05) if d & (d - 1) == 0 else prep.cayley(0.05 * _skew(d, seed))
+
+
+def test_fused_linear_on_the_rotated_input_is_the_original_linear():
+    # zh 2.2 / fr 2A: with h~ = h R, y = h W^T = h~ (W R)^T
+    rng = np.random.default_rng(70)
+    n, k = 5, 64
+    w = (rng.standard_normal((48, k)) * 0.02).astype(np.float32)
+    r = _orth(k, 71).astype(np.float32)
+    h = rng.standard_normal((n, k))
+    wt = prep.fuse_weight(w, right=r)
+    y = h @ w.astype(np.float64).T
+    y_fused = (h @ r.astype(np.float64)) @ wt.astype(np.float64).T
+    assert np.max(np.abs(y_fused - y)) <= 1e-5 * np.max(np.abs(y))
+    # an output basis R': y R' = h~ (R'^T W R)^T
+    r_out = _orth(48, 72).astype(np.float32)
+    wt2 = prep.fuse_weight(w, right=r, left=r_out)
+    y_out = (h @ r.astype(np.float64)) @ wt2.astype(np.float64).T
+    assert np.max(np.abs(y_out - y @ r_out.astype(np.float64))) <= 1e-5 * np.max(np.abs(y))
+
+
+def test_fusion_closed_forms():
+    rng = np.random.default_rng(73)
+    w = rng.standard_normal((32, 64)).astype(np.float32)
+    # identity rotations: the weight itself, bit for bit
+    assert np.array_equal(prep.fuse_weight(w, right=np.eye(64, dtype=np.float32)), w)
+    assert np.array_equal(prep.fuse_weight(w), w)
+    # a permutation on the right permutes the columns; on the left it permutes the rows
+    perm = rng.permutation(64)
+    p = np.eye(64, dtype=np.float32)[:, perm]
+    assert np.array_equal(prep.fuse_weight(w, right=p), w[:, perm])
+    q = np.eye(32, dtype=np.float32)[:, rng.permutation(32)]
+    assert np.array_equal(prep.fuse_weight(w, left=q), (q.T @ w).astype(np.float32))
+    # H is symmetric and orthogonal: fusing it twice gives the weight back
+    h = prep.hadamard(64).astype(np.float32)
+    twice = prep.fuse_weight(prep.fuse_weight(w, right=h), right=h)
+    assert np.max(np.abs(twice - w)) <= 1e-5 * np.max(np.abs(w))
+    # an orthogonal fusion keeps the Frobenius norm
+    wt = prep.fuse_weight(w, right=_orth(64, 74), left=_orth(32, 75))
+    assert abs(np.linalg.norm(wt.astype(np.float64)) / np.linalg.norm(w.astype(np.float64)) - 1) < 1e-6
