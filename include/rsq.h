@@ -11,14 +11,14 @@
  *    pointers; every other pointer is a device pointer on the current HIP
  *    device, at least 16-byte aligned. The library allocates nothing.
  *  - Workspace: the entry points that take `workspace, workspace_bytes` may
- *    need device scratch (partial sums and arrival counters of work split
- *    over workgroups), sized by the matching rsq_*_workspace_bytes query for
- *    the same sizes. A query result of 0 means NULL, 0 may be passed. The
- *    workspace must be zero-filled before its first use (once, e.g. right
- *    after allocation); every call leaves its counters at zero again, so a
- *    workspace serves any number of later calls without clearing. Calls that
- *    share a workspace must not run concurrently (enqueue them on one
- *    stream). Too small a workspace is RSQ_ERR_WORKSPACE.
+ *    need device scratch (for work split over workgroups whose partial
+ *    results meet through device memory), sized by the matching
+ *    rsq_*_workspace_bytes query for the same sizes; a result of 0 means
+ *    NULL, 0 may be passed. In this version every query returns 0: each
+ *    kernel keeps its exchanges inside a workgroup. A workspace, where one is
+ *    needed, is zero-filled before its first use and left zero-filled by
+ *    every call; calls that share one must not run concurrently (enqueue
+ *    them on one stream). Too small a workspace is RSQ_ERR_WORKSPACE.
  *  - Execution: work is enqueued on `stream` (a hipStream_t; NULL is the
  *    null stream) and the call returns without waiting. Device faults show
  *    at the caller's next synchronisation.
@@ -221,6 +221,23 @@ rsq_status rsq_qgemm_fp4(const uint8_t *a_fp4, const float *a_scales, int64_t n,
                          const float *w_scales, int64_t n_out, int64_t k, const void *residual, int64_t ld_r, void *y,
                          int y_dtype, int64_t ld_y, int32_t *acc_out, void *workspace, size_t workspace_bytes,
                          void *stream);
+
+/*
+ * Offline weight fusion (once per model, not per token): the pages fuse each
+ * block's rotations into its weights offline (zh 2.2, offline weight fusion,
+ * e.g. W~ = R^T W R; fr 2A, W~ = W R). For a linear y = h W^T whose input h
+ * lives in a basis rotated by R (h~ = h R), y = h~ (W R)^T; an output kept in
+ * a basis R' takes R'^T on the left. One call applies one side:
+ *   side RSQ_ROTATE_RIGHT: W_out = W R      (R: k x k)
+ *   side RSQ_ROTATE_LEFT:  W_out = R^T W    (R: n_out x n_out)
+ * W, W_out: n_out x k row-major float32; R row-major float32. Products and
+ * sums in float64, each output rounded once to float32. n_out and k multiples
+ * of 32, at most 2^20; W_out must not overlap W or R.
+ */
+#define RSQ_ROTATE_RIGHT 0
+#define RSQ_ROTATE_LEFT 1
+rsq_status rsq_rotate_weight(const float *W, int64_t n_out, int64_t k, const float *R, int side, float *W_out,
+                             void *stream);
 
 /*
  * One correction site feeding its quantised linear: rsq_correct_quant then

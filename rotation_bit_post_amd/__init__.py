@@ -12,5 +12,5 @@ from ._binding import (  # noqa: F401
     rsq_version, rsq_packed_row_bytes, rsq_site_bytes, rsq_site_prepare,
     rsq_qgemm_workspace_bytes, rsq_correct_workspace_bytes, rsq_layer_workspace_bytes, rsq_workspace,
     rsq_subspace_correct, rsq_quant_act, rsq_correct_quant, rsq_qgemm, rsq_qgemm_residual, rsq_layer_fused,
-    rsq_codes_to_fp4, rsq_qgemm_fp4,
+    rsq_codes_to_fp4, rsq_qgemm_fp4, rsq_rotate_weight, RSQ_ROTATE_RIGHT, RSQ_ROTATE_LEFT,
 )

@@ -18,6 +18,7 @@ RSQ_F32, RSQ_BF16 = 0, 1
 RSQ_QA_RMSNORM = 1
 RSQ_FP4 = 0x100          # bits = 3 | RSQ_FP4: 3-bit codes in the fp4 layout
 RSQ_MAX_RANK = 64
+RSQ_ROTATE_RIGHT, RSQ_ROTATE_LEFT = 0, 1
 
 
 class RsqError(RuntimeError):
@@ -55,6 +56,7 @@ def _load() -> C.CDLL:
         "rsq_layer_fused": (i32, [vp, vp, i32, i64, i64, vp, i32, vp, f32, i32, vp, vp, vp, vp, i64, vp, i32, vp, sz,
                                   vp]),
         "rsq_codes_to_fp4": (i32, [vp, i64, i64, vp, vp]),
+        "rsq_rotate_weight": (i32, [vp, i64, i64, vp, i32, vp, vp]),
         "rsq_qgemm_fp4": (i32, [vp, vp, i64, vp, vp, i64, i64, vp, i64, vp, i32, i64, vp, vp, sz, vp]),
     }
     for name, (res, args) in sig.items():
@@ -67,7 +69,7 @@ LIB = _load()
 EXPORTS = ("rsq_version", "rsq_status_str", "rsq_last_error", "rsq_packed_row_bytes", "rsq_site_bytes",
            "rsq_qgemm_workspace_bytes", "rsq_correct_workspace_bytes", "rsq_layer_workspace_bytes",
            "rsq_site_prepare", "rsq_subspace_correct", "rsq_quant_act", "rsq_correct_quant", "rsq_qgemm", "rsq_qgemm_residual",
-           "rsq_layer_fused", "rsq_codes_to_fp4", "rsq_qgemm_fp4")
+           "rsq_layer_fused", "rsq_codes_to_fp4", "rsq_qgemm_fp4", "rsq_rotate_weight")
 
 
 def _check(status: int, func: str) -> None:
@@ -370,3 +372,20 @@ def rsq_layer_fused(h_in, h_out, site, r: int, codes, scales, w_codes, w_scales,
     _check(LIB.rsq_layer_fused(_ptr(h_in), _ptr(h_out), _dtype_code(h_in), n, d, _ptr(site), r, _ptr(norm_w), eps,
                                bits, _ptr(codes), _ptr(scales), _ptr(w_codes), _ptr(w_scales), n_out, _ptr(y),
                                _dtype_code(y), ws, ws_bytes, _stream(stream)), "rsq_layer_fused")
+
+
+def rsq_rotate_weight(w, r, side: int, out, stream=None) -> None:
+    """Offline weight fusion: out = w r (side RSQ_ROTATE_RIGHT, r: k x k) or out = r^T w
+    (RSQ_ROTATE_LEFT, r: n x n); w, out: (n, k) float32, contiguous."""
+    import torch
+    _rows("w", w)
+    n, k = w.shape
+    _req(side in (RSQ_ROTATE_RIGHT, RSQ_ROTATE_LEFT), f"side = {side} is not RSQ_ROTATE_RIGHT or RSQ_ROTATE_LEFT")
+    rd = k if side == RSQ_ROTATE_RIGHT else n
+    _buffer("w", w, 4 * n * k, torch.float32)
+    _rows("r", r, rd, rd)
+    _buffer("r", r, 4 * rd * rd, torch.float32)
+    _rows("out", out, n, k)
+    _buffer("out", out, 4 * n * k, torch.float32)
+    _on_device(w=w, r=r, out=out)
+    _check(LIB.rsq_rotate_weight(_ptr(w), n, k, _ptr(r), side, _ptr(out), _stream(stream)), "rsq_rotate_weight")

@@ -21,7 +21,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "librsq.so")
-SOURCES = ["rsq_api.hip", "rsq_correct.hip", "rsq_quant.hip", "rsq_gemm.hip"]
+SOURCES = ["rsq_api.hip", "rsq_correct.hip", "rsq_quant.hip", "rsq_gemm.hip", "rsq_fuse.hip"]
 ARCH = "gfx950"
 
 

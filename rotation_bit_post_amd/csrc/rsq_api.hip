@@ -327,6 +327,28 @@ rsq_status rsq_qgemm_fp4(const uint8_t *a_fp4, const float *a_scales, int64_t n,
                       "rsq_qgemm_fp4 launch");
 }
 
+rsq_status rsq_rotate_weight(const float *W, int64_t n_out, int64_t k, const float *R, int side, float *W_out,
+                             void *stream) {
+    g_last_error[0] = 0;
+    RSQ_CHECK(side == RSQ_ROTATE_RIGHT || side == RSQ_ROTATE_LEFT, RSQ_ERR_INVALID_ARG,
+              "side = %d is not RSQ_ROTATE_RIGHT or RSQ_ROTATE_LEFT", side);
+    RSQ_CHECK(n_out > 0 && n_out % 32 == 0 && k > 0 && k % 32 == 0, RSQ_ERR_INVALID_ARG,
+              "n_out = %lld and k = %lld must be positive multiples of 32", (long long)n_out, (long long)k);
+    RSQ_CHECK(n_out <= (1 << 20) && k <= (1 << 20), RSQ_ERR_UNSUPPORTED, "n_out or k above 2^20");
+    RSQ_CHECK(W && R && W_out, RSQ_ERR_INVALID_ARG, "null pointer (W, R or W_out)");
+    RSQ_CHECK(aligned16(W) && aligned16(R) && aligned16(W_out), RSQ_ERR_INVALID_ARG,
+              "W, R and W_out must be 16-byte aligned");
+    const int64_t rd = side == RSQ_ROTATE_RIGHT ? k : n_out;
+    const char *w0 = reinterpret_cast<const char *>(W), *r0 = reinterpret_cast<const char *>(R);
+    const char *o0 = reinterpret_cast<const char *>(W_out);
+    const size_t wb = static_cast<size_t>(n_out) * k * 4, rb = static_cast<size_t>(rd) * rd * 4;
+    RSQ_CHECK((o0 + wb <= w0 || w0 + wb <= o0) && (o0 + wb <= r0 || r0 + rb <= o0), RSQ_ERR_INVALID_ARG,
+              "W_out overlaps W or R");
+    return hip_status(rsq::launch_rotate_weight(W, n_out, k, R, side == RSQ_ROTATE_LEFT, W_out,
+                                                static_cast<hipStream_t>(stream)),
+                      "rsq_rotate_weight launch");
+}
+
 rsq_status rsq_layer_fused(const void *h_in, void *h_out, int h_dtype, int64_t n, int64_t d, const void *site, int r,
                            const float *norm_w, float eps, int bits, uint8_t *codes, float *scales,
                            const uint8_t *w_codes, const float *w_scales, int64_t n_out, void *y, int y_dtype,

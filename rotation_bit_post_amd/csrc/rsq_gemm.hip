@@ -574,172 +574,13 @@ hipError_t launch_gemv16(const uint8_t *a, const float *sa, int64_t n, const uin
     return hipGetLastError();
 }
 
-template <int BITS, int TM, typename YT>
+template <int BITS, int TM, typename YT, int NW = 8>
 hipError_t launch_gemv(const uint8_t *a, const float *sa, int64_t n, const uint8_t *w, const float *sw, int64_t N,
                        int64_t K, void *y, int64_t ld_y, int32_t *acc_out, const void *res, int64_t ld_r,
                        hipStream_t s) {
-    constexpr int NW = 8;
     hipLaunchKernelGGL((qgemv_kernel<BITS, TM, NW, YT>), dim3(static_cast<unsigned>((N + 31) / 32)), dim3(NW * 64), 0,
                        s, a, sa, static_cast<int>(n), w, sw, static_cast<int>(N), static_cast<int>(K),
                        static_cast<YT *>(y), ld_y, acc_out, static_cast<const YT *>(res), ld_r);
-    return hipGetLastError();
-}
-
-// Split-k decode GEMM (n <= 64 tokens): a workgroup owns TN fragments of 32
-// output channels and all tokens (TM fragments of 32) over one range of k
-// steps; its NW waves take the steps of that range in turn, with operands
-// loaded straight from global memory into registers D steps ahead (no LDS, no
-// barrier in the k loop), and sum their accumulators through LDS in a fixed
-// order. With S > 1 the k steps of a channel tile are split over S
-// workgroups: each writes its int32 partial tile to the workspace and counts
-// itself in (release / acquire at device scope); the last to arrive adds the
-// S partials in split order - integer sums, so the result is exact whatever
-// the order of arrival - runs the epilogue and sets the counter back to zero.
-// More workgroups stream the weights, each with fewer k steps in flight, and
-// the activation rows each one reads shrink with its k range.
-template <int BITS, int TM, int TN, int NW, int D, typename YT>
-__global__ __launch_bounds__(NW * 64) void qgemm_splitk_kernel(const uint8_t *__restrict__ A,
-                                                               const float *__restrict__ sa, int n,
-                                                               const uint8_t *__restrict__ W,
-                                                               const float *__restrict__ sw, int N, int K, int S,
-                                                               YT *__restrict__ y, int64_t ld_y,
-                                                               int32_t *__restrict__ acc_out,
-                                                               const YT *__restrict__ res, int64_t ld_r,
-                                                               uint32_t *__restrict__ counters,
-                                                               int32_t *__restrict__ partials) {
-    using F = Fmt<BITS>;
-    constexpr int KSTEP_B = kBK * BITS / 8;   // packed bytes of one k step of a row
-    constexpr int TILE = TM * TN * 16 * 64;   // int32 accumulators of a workgroup
-    __shared__ int32_t red[NW][TILE];
-    __shared__ int last_arrival;
-    const int lane = threadIdx.x & 63;
-    const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
-    const int h = lane >> 5, l32 = lane & 31;
-    const int tile = blockIdx.x / S, split = blockIdx.x % S;
-    const int bn0 = tile * 32 * TN;
-    const uint32_t rb = static_cast<uint32_t>(K) * BITS / 8;
-    const int nkt = (K + kBK - 1) / kBK;
-    const int per = (nkt + S - 1) / S;                 // k steps per split
-    const int k0 = split * per, k1 = min(nkt, k0 + per);
-    const uint8_t *wrow[TN];
-#pragma unroll
-    for (int j = 0; j < TN; ++j) wrow[j] = W + static_cast<size_t>(min(bn0 + 32 * j + l32, N - 1)) * rb;
-    const uint8_t *arow[TM];
-#pragma unroll
-    for (int i = 0; i < TM; ++i) arow[i] = A + static_cast<size_t>(min(32 * i + l32, n - 1)) * rb;
-
-    Frag<BITS> fa[D][TM], fw[D][TN];
-    // lane half h takes codes [64h, 64h + 64) of a step; groups past the row
-    // end read the row's first group (in bounds) and their weight operand is
-    // zeroed before use; steps past the range reload the range's last step
-    auto load_step = [&](int kt, int slot) {
-        kt = min(kt, k1 - 1);
-        const int kk = kt * kBK + 64 * h;
-        const uint32_t off0 = kk < K ? static_cast<uint32_t>(kt) * KSTEP_B + h * (KSTEP_B / 2) : 0u;
-        const uint32_t off1 = kk + 32 < K ? static_cast<uint32_t>(kt) * KSTEP_B + h * (KSTEP_B / 2) + F::kGroupB : 0u;
-#pragma unroll
-        for (int j = 0; j < TN; ++j) fw[slot][j].load2(wrow[j] + off0, wrow[j] + off1);
-#pragma unroll
-        for (int i = 0; i < TM; ++i) fa[slot][i].load2(arow[i] + off0, arow[i] + off1);
-    };
-    v16i acc[TM][TN];
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0;
-    auto compute = [&](int kt, int slot) {
-        if (kt >= k1) return;
-#pragma unroll
-        for (int s = 0; s < kBK / 32; ++s) {
-            const bool live = kt * kBK + 64 * h + 32 * (s >> 1) < K;
-            v4i wo[TN];
-#pragma unroll
-            for (int j = 0; j < TN; ++j) wo[j] = live ? fw[slot][j].op(s) : v4i{0, 0, 0, 0};
-#pragma unroll
-            for (int i = 0; i < TM; ++i) {
-                const v4i ao = fa[slot][i].op(s);
-#pragma unroll
-                for (int j = 0; j < TN; ++j) acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ao, wo[j], acc[i][j], 0, 0, 0);
-            }
-        }
-    };
-    // a ring of D register slots: slot u holds step kt + u NW while the steps
-    // before it are multiplied
-#pragma unroll
-    for (int u = 0; u < D; ++u) load_step(k0 + w + u * NW, u);
-    for (int kt = k0 + w; kt < k1; kt += D * NW) {
-#pragma unroll
-        for (int u = 0; u < D; ++u) {
-            compute(kt + u * NW, u);
-            load_step(kt + (u + D) * NW, u);
-        }
-    }
-
-    // the waves' partial accumulators, summed in a fixed order; element e of
-    // the tile is fragment (i, j) = e / 1024, register v = (e / 64) % 16, lane e % 64
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) red[w][((i * TN + j) * 16 + v) * 64 + lane] = acc[i][j][v];
-    __syncthreads();
-    if (S > 1) {
-        int32_t *mine = partials + (static_cast<size_t>(tile) * S + split) * TILE;
-        for (int e = threadIdx.x; e < TILE; e += NW * 64) {
-            int a = 0;
-#pragma unroll
-            for (int ww = 0; ww < NW; ++ww) a += red[ww][e];
-            mine[e] = a;
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-        __syncthreads();
-        if (threadIdx.x == 0) {
-            const uint32_t before = __hip_atomic_fetch_add(counters + tile, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-            last_arrival = before == static_cast<uint32_t>(S - 1);
-        }
-        __syncthreads();
-        if (!last_arrival) return;
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    }
-    for (int e = threadIdx.x; e < TILE; e += NW * 64) {
-        int a = 0;
-        if (S > 1) {
-            const int32_t *parts = partials + static_cast<size_t>(tile) * S * TILE + e;
-            for (int sp = 0; sp < S; ++sp) a += parts[static_cast<size_t>(sp) * TILE];
-        } else {
-#pragma unroll
-            for (int ww = 0; ww < NW; ++ww) a += red[ww][e];
-        }
-        const int f = e / 1024, v = (e / 64) % 16, ln = e % 64;
-        const int i = f / TN, j = f % TN;
-        const int tok = 32 * i + 8 * (v >> 2) + 4 * (ln >> 5) + (v & 3);
-        const int ch = bn0 + 32 * j + (ln & 31);
-        if (tok < n && ch < N) {
-            a >>= F::kShift;
-            float val = (static_cast<float>(a) * sa[tok]) * sw[ch];
-            if (res != nullptr) val += from_out(res[static_cast<int64_t>(tok) * ld_r + ch]);
-            y[static_cast<int64_t>(tok) * ld_y + ch] = to_out<YT>(val);
-            if (acc_out != nullptr) acc_out[static_cast<int64_t>(tok) * N + ch] = a;
-        }
-    }
-    if (S > 1 && threadIdx.x == 0) __hip_atomic_store(counters + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-template <int BITS, int TM, int TN, int NW, int D, typename YT>
-hipError_t launch_splitk(const uint8_t *a, const float *sa, int64_t n, const uint8_t *w, const float *sw, int64_t N,
-                         int64_t K, int S, void *y, int64_t ld_y, int32_t *acc_out, const void *res, int64_t ld_r,
-                         void *ws, hipStream_t s) {
-    const int64_t tiles = (N + 32 * TN - 1) / (32 * TN);
-    uint32_t *counters = static_cast<uint32_t *>(ws);
-    int32_t *partials = reinterpret_cast<int32_t *>(static_cast<uint8_t *>(ws) + kCounterBytes);
-    if (S > 1 && (ws == nullptr || tiles > kMaxCounters)) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((qgemm_splitk_kernel<BITS, TM, TN, NW, D, YT>), dim3(static_cast<unsigned>(tiles * S)),
-                       dim3(NW * 64), 0, s, a, sa, static_cast<int>(n), w, sw, static_cast<int>(N),
-                       static_cast<int>(K), S, static_cast<YT *>(y), ld_y, acc_out, static_cast<const YT *>(res), ld_r,
-                       S > 1 ? counters : nullptr, S > 1 ? partials : nullptr);
     return hipGetLastError();
 }
 
@@ -902,6 +743,12 @@ hipError_t launch_b(const uint8_t *a, const float *sa, int64_t n, const uint8_t 
         // long k: more k steps in flight (up to 16 tokens: 4 waves with a
         // 3-step ring, e.g. 1 token at K = 11008: 6.5 against 7.5 us for 8
         // waves with 2; more tokens: 8 waves with 2)
+        // up to 16 tokens on a layer wide enough for more than four rounds of
+        // 16-channel workgroups: 32-channel workgroups of 4 waves instead
+        // (gate|up, 22016 x 4096: 8 tokens 13.5 against 14.6 us, 16 tokens 15.1
+        // against 16.8 us; equal at 1 token)
+        if (n <= 16 && N / 16 > 4 * cus && K < 8192)
+            return launch_gemv<BITS, 1, YT, 4>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s);
         if (n <= 16 || (n <= 64 && N / 16 <= cus)) {
             const bool deep = K >= 8192;
             switch ((n + 15) / 16) {
@@ -983,7 +830,7 @@ hipError_t launch_codes_to_fp4(const uint8_t *codes, int64_t rows, int64_t k, ui
 hipError_t launch_qgemm(const uint8_t *a, const float *sa, int64_t n, const uint8_t *w, const float *sw,
                         int64_t n_out, int64_t k, int bits, void *y, int y_dtype, int64_t ld_y,
                         int32_t *acc_out, const void *res, int64_t ld_r, void *ws, hipStream_t s) {
-    (void)ws;
+    (void)ws;   // see qgemm_workspace_bytes
     if (bits == kFp4) {
         if (y_dtype == 1) return launch_b<kFp4, uint16_t>(a, sa, n, w, sw, n_out, k, y, ld_y, acc_out, res, ld_r, s);
         return launch_b<kFp4, float>(a, sa, n, w, sw, n_out, k, y, ld_y, acc_out, res, ld_r, s);
@@ -997,6 +844,10 @@ hipError_t launch_qgemm(const uint8_t *a, const float *sa, int64_t n, const uint
 }
 
 size_t qgemm_workspace_bytes(int64_t n, int64_t n_out, int64_t k, int bits) {
+    // no GEMM kernel splits its k range over workgroups: a split whose partial
+    // sums meet through device memory needs device-scope release and acquire
+    // fences, which write back or invalidate the whole L2 of an XCD, and
+    // measured 3-4 times slower than the single-workgroup decode kernels
     (void)n; (void)n_out; (void)k; (void)bits;
     return 0;
 }

@@ -13,14 +13,6 @@ inline int rank_pad(int r) { return (r + 31) / 32 * 32; }
 // (parts U hi, V hi, U lo, V lo).
 inline size_t site_bytes(int64_t d, int r) { return static_cast<size_t>(d) * rank_pad(r) * 2 * 2 * 2; }
 
-// Workspace layout shared by every kernel that takes one: arrival counters
-// (uint32) in the first kCounterBytes, zero between calls (each kernel returns
-// the counters it used to zero), so one workspace serves kernels that run one
-// after another on a stream; partial sums after them, always written before
-// they are read.
-constexpr size_t kCounterBytes = 16384;
-constexpr int kMaxCounters = static_cast<int>(kCounterBytes / 4);
-
 // Code formats (the launchers' `bits`): packed int4 (4), packed int3 (3), and
 // 3-bit codes held as fp4 e2m1 nibbles (kFp4).
 constexpr int kFp4 = 1;
@@ -53,35 +45,37 @@ hipError_t launch_site_prepare(const float *U, const float *M, int d, int r, voi
 
 // h_dtype: 0 float32, 1 bfloat16. quant: also RMSNorm + quantise + pack
 // (bits: 4, 3 or kFp4, the format of the codes written). ws: device scratch
-// of at least correct_workspace_bytes(n, d) bytes (zero-filled before its
-// first use, left zero-filled), or NULL when that is 0.
+// of at least correct_workspace_bytes(n, d) bytes, or NULL when that is 0.
 hipError_t launch_correct(const void *h_in, void *h_out, int h_dtype, int64_t n, int d, int64_t ld_h,
                           const void *site, int r, bool quant, const float *norm_w, float eps, int bits,
                           uint8_t *codes, float *scales, void *ws, hipStream_t s);
 
-// Scratch bytes the quantising correction may need for n tokens of width d
-// (the arrival counters of the small-batch form, whose workgroups split the
-// columns of a token block and whose last one quantises the block).
+// Scratch bytes the quantising correction needs for n tokens of width d
+// (0: no correction kernel exchanges data between workgroups).
 size_t correct_workspace_bytes(int64_t n, int64_t d);
 
 hipError_t launch_quant(const void *x, int x_dtype, int64_t n, int k, int64_t ld_x, bool norm,
                         const float *norm_w, float eps, int bits, uint8_t *codes, float *scales,
                         hipStream_t s);
 
+// Offline weight fusion: out = W R (R: k x k) or, with left, out = R^T W (R: n x n);
+// W and out: n x k row-major float32.
+hipError_t launch_rotate_weight(const float *W, int64_t n, int64_t k, const float *R, bool left, float *out,
+                                hipStream_t s);
+
 // Packed int3 rows (k codes each) -> fp4 rows (k / 2 bytes each).
 hipError_t launch_codes_to_fp4(const uint8_t *codes, int64_t rows, int64_t k, uint8_t *out, hipStream_t s);
 
 // res: NULL, or n rows of n_out values of the output type (stride ld_r) added
 // to the dequantised result before its rounding. bits: 4, 3 or kFp4. ws:
-// device scratch of at least qgemm_workspace_bytes(n, n_out, k, bits) bytes
-// (zero-filled before its first use, left zero-filled), or NULL when that is 0.
+// device scratch of at least qgemm_workspace_bytes(n, n_out, k, bits) bytes,
+// or NULL when that is 0.
 hipError_t launch_qgemm(const uint8_t *a, const float *sa, int64_t n, const uint8_t *w, const float *sw,
                         int64_t n_out, int64_t k, int bits, void *y, int y_dtype, int64_t ld_y,
                         int32_t *acc_out, const void *res, int64_t ld_r, void *ws, hipStream_t s);
 
-// Scratch bytes of the GEMM launch for these sizes (the int32 partial sums and
-// arrival counters of a k range split over workgroups); 0 when the kernel the
-// launcher picks splits nothing over workgroups. bits: 4, 3 or kFp4.
+// Scratch bytes of the GEMM launch for these sizes (0: no GEMM kernel splits
+// its k range over workgroups). bits: 4, 3 or kFp4.
 size_t qgemm_workspace_bytes(int64_t n, int64_t n_out, int64_t k, int bits);
 
 }  // namespace rsq

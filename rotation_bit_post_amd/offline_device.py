@@ -89,3 +89,20 @@ def convert_site_device(r_in, r_out, r: int, tol: float = 1e-10, max_iters: int 
         raise ValueError(f"no singular-value gap at rank {r}")
     m = vec.T @ t @ vec - torch.eye(r, dtype=torch.float64, device=dev)
     return (vec.to(torch.float32).cpu().numpy(), m.to(torch.float32).cpu().numpy(), it, res)
+
+
+def fuse_weight_device(w, right=None, left=None):
+    """W~ = left^T W right on the device with the library's rotation kernel (one launch per side,
+    float64 sums, one float32 rounding per side); w, right, left: float32 device tensors."""
+    import torch
+    from . import _binding as B
+    out = w
+    if right is not None:
+        nxt = torch.empty_like(w)
+        B.rsq_rotate_weight(out, right, B.RSQ_ROTATE_RIGHT, nxt)
+        out = nxt
+    if left is not None:
+        nxt = torch.empty_like(w)
+        B.rsq_rotate_weight(out, left, B.RSQ_ROTATE_LEFT, nxt)
+        out = nxt
+    return out

@@ -16,6 +16,7 @@ const void *g_res = nullptr;
 int64_t g_ld_r = -1;
 int g_bits = -1;
 void *g_ws = nullptr;
+bool g_left = false;
 size_t g_need_c = 0, g_need_g = 0;
 int g_fail = 0, g_cases = 0;
 
@@ -62,6 +63,11 @@ hipError_t launch_qgemm(const uint8_t *, const float *, int64_t, const uint8_t *
 }
 hipError_t launch_codes_to_fp4(const uint8_t *, int64_t, int64_t, uint8_t *, hipStream_t) {
     ++g_launches;
+    return g_ret;
+}
+hipError_t launch_rotate_weight(const float *, int64_t, int64_t, const float *, bool left, float *, hipStream_t) {
+    ++g_launches;
+    g_left = left;
     return g_ret;
 }
 }  // namespace rsq
@@ -192,6 +198,24 @@ int main() {
     expect("correct_quant norm_w misaligned", rsq_correct_quant(p, q, RSQ_BF16, 4, 256, p, 8, f + 2, 1e-5f, 4, q + 4096, fo + 4096, nullptr, 0, nullptr), RSQ_ERR_INVALID_ARG, 0);
     expect("layer_fused norm_w misaligned", rsq_layer_fused(p, q, RSQ_BF16, 4, 256, p, 8, f + 3, 1e-5f, 4, q + 4096, fo + 4096, p, f, 64, q + 8192, RSQ_BF16, nullptr, 0, nullptr), RSQ_ERR_INVALID_ARG, 0);
     expect("quant norm_w aligned", rsq_quant_act(p, RSQ_BF16, 4, 256, 256, RSQ_QA_RMSNORM, f + 4, 1e-5f, 4, q, fo, nullptr), RSQ_OK, 1);
+
+    // offline weight fusion
+    {
+        const float *wf = reinterpret_cast<const float *>(p);
+        float *wo = reinterpret_cast<float *>(q);
+        const float *rf = reinterpret_cast<const float *>(q + 65536);
+        expect("rotate right", rsq_rotate_weight(wf, 64, 96, rf, RSQ_ROTATE_RIGHT, wo, nullptr), RSQ_OK, 1);
+        if (g_left) { std::printf("FAIL rotate right reached the launcher as left\n"); ++g_fail; }
+        expect("rotate left", rsq_rotate_weight(wf, 64, 96, rf, RSQ_ROTATE_LEFT, wo, nullptr), RSQ_OK, 1);
+        if (!g_left) { std::printf("FAIL rotate left reached the launcher as right\n"); ++g_fail; }
+        expect("rotate side", rsq_rotate_weight(wf, 64, 96, rf, 2, wo, nullptr), RSQ_ERR_INVALID_ARG, 0);
+        expect("rotate k", rsq_rotate_weight(wf, 64, 100, rf, RSQ_ROTATE_RIGHT, wo, nullptr), RSQ_ERR_INVALID_ARG, 0);
+        expect("rotate null", rsq_rotate_weight(wf, 64, 96, nullptr, RSQ_ROTATE_RIGHT, wo, nullptr), RSQ_ERR_INVALID_ARG, 0);
+        expect("rotate in place", rsq_rotate_weight(wf, 64, 96, rf, RSQ_ROTATE_RIGHT, const_cast<float *>(wf), nullptr), RSQ_ERR_INVALID_ARG, 0);
+        expect("rotate overlaps R", rsq_rotate_weight(wf, 64, 96, rf, RSQ_ROTATE_RIGHT, wo + 16384, nullptr), RSQ_ERR_INVALID_ARG, 0);
+        expect("rotate misaligned", rsq_rotate_weight(wf + 1, 64, 96, rf, RSQ_ROTATE_RIGHT, wo, nullptr), RSQ_ERR_INVALID_ARG, 0);
+        expect("rotate too large", rsq_rotate_weight(wf, 64, (1 << 20) + 32, rf, RSQ_ROTATE_RIGHT, wo, nullptr), RSQ_ERR_UNSUPPORTED, 0);
+    }
 
     // a launch failure surfaces as RSQ_ERR_HIP with a message; the fused call stops after the failed launch
     g_ret = hipErrorInvalidValue;

@@ -554,33 +554,30 @@ SMALL_SITE_CASES = [  # dtype, d, r, n, bits, weighted: batches small enough for
 
 @pytest.mark.parametrize("dtype,d,r,n,bits,weighted", SMALL_SITE_CASES)
 def test_small_batch_site_matches_oracle_and_the_two_step_form(dtype, d, r, n, bits, weighted):
-    """A few tokens: the column-split correction whose last workgroup per token
-    block quantises the block (one launch, counters in the workspace). h' equals
-    the correction alone bit for bit; codes and scales match the oracle
-    quantiser on the GPU's own h'; a second call on the same workspace (its
-    counters back at zero) repeats the first exactly."""
+    """A few tokens: the column-split correction (workgroups split the columns
+    of each token block), then the standalone quantiser on the stored rows. h'
+    equals the correction alone bit for bit; codes and scales match the oracle
+    quantiser on the GPU's own h'; a second call repeats the first exactly."""
     rsq = lib()
     import torch
     print(f"case small site dtype={dtype} d={d} r={r} n={n} bits={bits} w={weighted}", flush=True)
-    assert rsq.rsq_correct_workspace_bytes(n, d) > 0
+    assert rsq.rsq_correct_workspace_bytes(n, d) == 0
     U, M = random_site(d, r, seed=d + n) if d <= 2048 else subspace_site(d, r, seed=d + n)
     site = gpu_site(U, M)
     h = residual(n, d, dtype, seed=n + 5)
     w = np.random.default_rng(n).uniform(0.5, 1.5, d).astype(np.float32) if weighted else None
     wd = None if w is None else to_dev(w, "f32")
     hd = to_dev(h, dtype)
-    ws = rsq.rsq_workspace(rsq.rsq_correct_workspace_bytes(n, d))
     rb = rsq.rsq_packed_row_bytes(d, bits)
     outs = []
     for _ in range(2):
         h1, c1, s1 = torch.empty_like(hd), empty_u8(n, rb), empty_f32(n)
-        rsq.rsq_correct_quant(hd, h1, site, r, c1, s1, bits, norm_w=wd, workspace=ws)
+        rsq.rsq_correct_quant(hd, h1, site, r, c1, s1, bits, norm_w=wd)
         outs.append((h1, c1, s1))
     h2 = torch.empty_like(hd)
     rsq.rsq_subspace_correct(hd, h2, site, r)
     torch.cuda.synchronize()
     assert all(torch.equal(a, b) for a, b in zip(outs[0], outs[1]))
-    assert not ws.any()                                   # every counter back at zero
     h1, c1, s1 = outs[0]
     assert torch.equal(h1, h2)
     hp = to_host(h1)
