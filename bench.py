@@ -59,6 +59,10 @@ def parse():
                    help="only run a plain device copy of MIB MiB (calibrates rocprofv3 byte counters) and exit")
     p.add_argument("--mha", action="store_true", help="all-D x D q/k/v projections instead of the GQA shapes")
     p.add_argument("--no-decode", action="store_true", help="skip the decode-size leg (1, 8 and 64 tokens)")
+    p.add_argument("--no-workload-legs", action="store_true",
+                   help="skip the short legs of the LLaMA-3-8B and LLaMA-2-70B workloads in the default run")
+    p.add_argument("--cpu-one-core", action="store_true",
+                   help="also time the CPU oracle on one thread (one whole pass; slow)")
     return p.parse_args()
 
 
@@ -294,7 +298,7 @@ def measured_traffic(name: str, src_hash: str):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(path, n_sample: int, min_s: float = 10.0):
+def cpu_baseline(path, n_sample: int, min_s: float = 10.0, threads: int = 0):
     """The CPU oracle (unchanged) on the first n_sample tokens of the same workload."""
     import numpy as np
     from oracle import online
@@ -308,7 +312,7 @@ def cpu_baseline(path, n_sample: int, min_s: float = 10.0):
     o_in = G.linear_input(cfg, "o_in", n_sample, cfg.D)
     down_in = G.linear_input(cfg, "down_in", n_sample, cfg.F)
     # the host's share of cores (OMP_NUM_THREADS where it is set, else every core)
-    limit = int(os.environ.get("OMP_NUM_THREADS") or 0) or os.cpu_count()
+    limit = threads or int(os.environ.get("OMP_NUM_THREADS") or 0) or os.cpu_count()
     with threadpoolctl.threadpool_limits(limits=limit):
         info = threadpoolctl.threadpool_info()
         threads = max([i.get("num_threads", 1) for i in info] or [1])
@@ -327,11 +331,12 @@ def cpu_baseline(path, n_sample: int, min_s: float = 10.0):
                       f"float64 numpy; {passes} pass(es) in {dt:.1f} s wall"}
 
 
-def decode_leg(sites, ns=(1, 8, 64), copies: int = 3, iters: int = 100):
+def decode_leg(sites, ns=(1, 8, 64), copies: int = 12, iters: int = 200):
     """The decode workload (the same layer at 1, 8 and 64 tokens, the prefill workload's
     sites, weights and leading residual rows): one step, and each stage, as replayed HIP
-    graphs - an eager decode step is bound by the host's launch rate, not the GPU. Three
-    copies of every buffer rotate (more than the 256 MB Infinity Cache of weights)."""
+    graphs - an eager decode step is bound by the host's launch rate, not the GPU. Twelve
+    copies of every buffer rotate, so that even one stage's weights (25 MB for q|k|v)
+    come back to the same copy only after more than the 256 MB Infinity Cache."""
     import torch
     import synth
     from rotation_bit_post_amd.path import LayerPath
@@ -354,15 +359,18 @@ def decode_leg(sites, ns=(1, 8, 64), copies: int = 3, iters: int = 100):
         torch.cuda.synchronize()
         same = all(torch.equal(v, ref[k]) for k, v in base.outputs().items())
         ms_step = replay_ms(graphs, iters, stream)
-        # each stage alone: a graph of 10 launches per buffer copy
+        # each stage cold and alone: one graph launching the stage once for each buffer
+        # copy in turn, so that between two launches on the same weights come the other
+        # copies' (more than the 256 MB Infinity Cache); time per launch, dispatch included
         stages = {}
         gemm_bytes = gemm_ms = 0.0
         names = [nm for nm, _, _ in base.stages()]
         for j, nm in enumerate(names):
-            g = [capture([p.stages()[j][2]], reps=10) for p in paths]
-            ms = replay_ms(g, max(10, iters // 5), stream) / 10
+            g = capture([p.stages()[j][2] for p in paths])
+            ms = replay_ms([g], max(20, iters // 4), stream) / len(paths)
             byts, ops = base.stage_work(nm)
-            stages[nm] = {"ms": round(ms, 5), "alg_bytes": byts, "hbm_frac": round(byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+            stages[nm] = {"ms": round(ms, 5), "alg_bytes": byts,
+                          "hbm_frac": round(byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
             if ops:
                 gemm_bytes += byts
                 gemm_ms += ms
@@ -376,10 +384,82 @@ def decode_leg(sites, ns=(1, 8, 64), copies: int = 3, iters: int = 100):
         }
         del paths, graphs, base
         torch.cuda.empty_cache()
-    out["note"] = ("decode-size batches of the same layer (llama2-7b shapes, W4A4), steps and stages replayed as HIP "
-                   "graphs; stage times include the graph's per-launch dispatch; hbm_frac = algorithmic bytes / time / "
-                   "8 TB/s")
+    out["note"] = ("decode-size batches of the same layer (llama2-7b shapes, W4A4), replayed as HIP graphs over twelve "
+                   "buffer copies, cold: a step, and each stage alone launched once per copy in turn (time per "
+                   "launch, graph dispatch included); hbm_frac = algorithmic bytes / time / 8 TB/s")
     return out
+
+
+def timing_sites(d: int, r: int, seed: int = 0):
+    """Seeded sites of the right shapes for a timing run: U an orthonormal d x r basis (QR of a Gaussian
+    matrix), M = C - I_r for a Cayley rotation C of r x r. The kernels' work does not depend on the values,
+    and these need no d x d solve (minutes on the host at d = 8192)."""
+    from rotation_bit_post_amd.offline import cayley_rotation
+    out = {}
+    for i, which in enumerate(("A", "B")):
+        rng = np.random.default_rng([seed, i])
+        u, _ = np.linalg.qr(rng.standard_normal((d, r)))
+        g = np.triu(rng.standard_normal((r, r)), 1)
+        m = cayley_rotation(g - g.T, 0.3) - np.eye(r)
+        out[which] = (u.astype(np.float32), m.astype(np.float32))
+    return out
+
+
+def workload_leg(wl, steps: int = 10):
+    """A short run of another prefill workload (its weights and batch, seeded timing sites of its shapes):
+    eager steps over two buffer copies, events between stages for the GEMMs' matrix-core fraction and
+    the sites' HBM fraction."""
+    import torch
+    import synth
+    from rotation_bit_post_amd.path import LayerPath
+    progress(f"workload leg: {wl}")
+    cfg = synth.workload(wl)
+    base = LayerPath.build(wl, sites=timing_sites(cfg.D, cfg.r))
+    paths = [base, base.clone()]
+    lists = [p.stages() for p in paths]
+    stream = torch.cuda.current_stream()
+    t0, i = time.perf_counter(), 0
+    while i < 3 or time.perf_counter() - t0 < 0.25:
+        for _, _, fn in lists[i % 2]:
+            fn()
+        i += 1
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(steps):
+        for _, _, fn in lists[i % 2]:
+            fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    names = [nm for nm, _, _ in lists[0]]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(steps)]
+    for i in range(steps):
+        ev[i][0].record(stream)
+        for j, (_, _, fn) in enumerate(lists[i % 2]):
+            fn()
+            ev[i][j + 1].record(stream)
+    torch.cuda.synchronize()
+    peak = FP4_PEAK_TOPS if base.fp4 else INT8_PEAK_TOPS
+    stages, g_ops, g_ms = {}, 0, 0.0
+    for j, nm in enumerate(names):
+        t = sum(ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(steps)) / steps
+        byts, ops = base.stage_work(nm)
+        rec = {"ms": round(t, 5), "hbm_frac": round(byts / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        if ops:
+            rec["mfma_frac"] = round(ops / (t * 1e-3) / 1e12 / peak, 4)
+            g_ops += ops
+            g_ms += t
+        stages[nm] = rec
+    cfg = base.cfg
+    res = {"tokens": base.n, "ms_per_step": round(ms, 5), "tokens_per_s": round(base.n / (ms * 1e-3), 1),
+           "gemm_frac_of_peak": round(g_ops / (g_ms * 1e-3) / 1e12 / peak, 4), "peak_tops": peak,
+           "dtype": "fp4" if base.fp4 else "int8", "stages": stages,
+           "shapes": f"D={cfg.D}, FFN={cfg.F}, r={base.r}, W{cfg.bits}A{cfg.bits}, q|k|v {base.linears['qkv'].N}",
+           "sites": "seeded orthonormal subspace sites of the workload's shapes (timing only)"}
+    del paths, lists, base
+    torch.cuda.empty_cache()
+    return res
 
 
 def main():
@@ -437,6 +517,18 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_eager = e0.elapsed_time(e1) / args.steps
+
+    # warm: one buffer set only, so a step finds its inputs in the Infinity Cache
+    for _, _, fn in stage_lists[0]:
+        fn()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(args.steps):
+        for _, _, fn in stage_lists[0]:
+            fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_warm = e0.elapsed_time(e1) / args.steps
 
     # 2. the same step as a replayed HIP graph (one per buffer copy), used only
     #    if its outputs are bit-identical to the eager step's
@@ -551,10 +643,17 @@ def main():
     value = n / (ms_per_step * 1e-3)
     decode_sized = n <= 64
     if decode_sized:
-        # a few tokens: the GEMMs stream their weights once, so HBM bounds them
-        gemm_bytes = sum(stages_out[nm]["alg_bytes"] for nm in names if kinds[nm] == "gemm")
+        # a few tokens: the GEMMs stream their weights once, so HBM bounds them. An eager
+        # step of this size is bound by the host's launch rate, so the GEMM times come
+        # from replayed graphs, each stage cold (decode_leg)
+        sites = {w: (st.U.cpu().numpy(), st.M.cpu().numpy()) for w, st in base.sites.items()}
+        leg = decode_leg(sites, ns=(n,))
+        gemm_nm = [nm for nm in names if kinds[nm] == "gemm"]
+        gemm_bytes = sum(leg[str(n)]["stages"][nm]["alg_bytes"] for nm in gemm_nm)
+        gemm_ms = sum(leg[str(n)]["stages"][nm]["ms"] for nm in gemm_nm)
         achieved = gemm_bytes / (gemm_ms * 1e-3) / 1e9
-        roofline = {"kernel": "the four quantised-linear launches of a step (weights streamed once)", "bound": "hbm",
+        roofline = {"kernel": "the four quantised-linear launches of a step (weights streamed once; each timed cold "
+                              "in a replayed graph)", "bound": "hbm",
                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                     "avg_launch_ms": round(gemm_ms / max(gemm_launches, 1), 5)}
@@ -610,13 +709,16 @@ def main():
         },
         "timing": {
             "ms_per_step_eager": round(ms_eager, 5),
+            "ms_per_step_eager_warm": round(ms_warm, 5),
             "ms_per_step_graph": None if ms_graph is None else round(ms_graph, 5),
             "graph_outputs_identical": graph_ok,
             "value_from": "graph" if ms_per_step != ms_eager else "eager",
             "step_ms_p10_p50_p90": [pct(0.1), pct(0.5), pct(0.9)],
             "note": "eager: the step's launches back to back; graph: the same launches recorded once as a HIP "
                     "graph and replayed (outputs checked bit-identical first); value uses the faster; "
-                    "percentiles: single steps of the per-stage pass (events between stages add a little)",
+                    "percentiles: single steps of the per-stage pass (events between stages add a little); "
+                    "warm: one buffer set, inputs left in the 256 MB Infinity Cache by the previous step (cold, "
+                    "the value: buffer copies alternate)",
         },
         "offline_prep": base.prep_info,
         "wall_s_timed": round(wall, 3),
@@ -626,12 +728,19 @@ def main():
     if not args.no_dense and "A" in base.mismatch:
         progress("dense h T comparator")
         out["dense_T_comparator"] = dense_comparator(base)
+    if decode_sized:
+        out["decode"] = leg
     if not args.no_decode and cfg.name == "llama2-7b-prefill-w4a4":
         sites = {w: (st.U.cpu().numpy(), st.M.cpu().numpy()) for w, st in base.sites.items()}
         out["decode"] = decode_leg(sites)
+    if not args.no_workload_legs and cfg.name == "llama2-7b-prefill-w4a4":
+        out["other_workloads"] = {wl: workload_leg(wl) for wl in ("llama3-8b-prefill-w3a3", "llama2-70b-prefill-w4a4")}
     if not args.no_cpu_baseline:
         progress(f"CPU oracle on a {min(args.cpu_sample, n)}-token sample")
         out["cpu_baseline"] = cpu_baseline(base, min(args.cpu_sample, n))
+        if args.cpu_one_core:
+            progress("CPU oracle on one thread")
+            out["cpu_baseline_one_core"] = cpu_baseline(base, min(args.cpu_sample, n), min_s=0.0, threads=1)
     print(json.dumps(out), flush=True)
 
 

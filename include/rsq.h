@@ -157,8 +157,12 @@ rsq_status rsq_quant_act(const void *x, int x_dtype, int64_t n, int64_t k, int64
  * rsq_subspace_correct's; the sum of squares is taken in another order
  * (bfloat16 squares summed by 8 in float32, exactly per product, then in
  * float64), so scales may differ from rsq_quant_act's by a few ulps and codes
- * only where a / s lies that close to a rounding tie.
- * h_in, h_out: contiguous rows (stride d).
+ * only where a / s lies that close to a rounding tie. Batches too small to
+ * fill the GPU with token blocks (not in place) run as two launches: the
+ * correction split over the columns, then rsq_quant_act's kernel on the
+ * stored rows (its results exactly).
+ * h_in, h_out: contiguous rows (stride d). workspace: see Conventions
+ * (rsq_correct_workspace_bytes).
  */
 rsq_status rsq_correct_quant(const void *h_in, void *h_out, int h_dtype, int64_t n, int64_t d,
                              const void *site, int r, const float *norm_w, float eps, int bits,
@@ -172,7 +176,9 @@ rsq_status rsq_correct_quant(const void *h_in, void *h_out, int h_dtype, int64_t
  *   y[t, j]   = (float32(acc[t, j]) * a_scales[t]) * w_scales[j]   (float32), then y_dtype
  * a_codes: n packed rows of k codes; w_codes: n_out packed rows of k codes.
  * y: n rows, stride ld_y (>= n_out). acc_out: NULL, or n x n_out int32
- * (contiguous) that receives the raw accumulators.
+ * (contiguous) that receives the raw accumulators. workspace: see
+ * Conventions (rsq_qgemm_workspace_bytes; also for rsq_qgemm_residual and
+ * rsq_qgemm_fp4).
  */
 rsq_status rsq_qgemm(const uint8_t *a_codes, const float *a_scales, int64_t n,
                      const uint8_t *w_codes, const float *w_scales, int64_t n_out,
@@ -242,6 +248,8 @@ rsq_status rsq_rotate_weight(const float *W, int64_t n_out, int64_t k, const flo
 /*
  * One correction site feeding its quantised linear: rsq_correct_quant then
  * rsq_qgemm on its codes. Writes h_out, codes, scales and y (stride n_out).
+ * workspace: see Conventions (rsq_layer_workspace_bytes; the two stages run
+ * one after the other and share it).
  */
 rsq_status rsq_layer_fused(const void *h_in, void *h_out, int h_dtype, int64_t n, int64_t d,
                            const void *site, int r, const float *norm_w, float eps, int bits,
