@@ -30,6 +30,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+ALONE_COPIES = 16           # buffer copies the stage-alone pass rotates over
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix-core peak
 INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 matrix-core peak
 FP4_PEAK_TOPS = 10100.0        # MI355X dense fp4 (and fp6) matrix-core peak
@@ -61,8 +62,8 @@ def parse():
     p.add_argument("--no-decode", action="store_true", help="skip the decode-size leg (1, 8 and 64 tokens)")
     p.add_argument("--no-workload-legs", action="store_true",
                    help="skip the short legs of the LLaMA-3-8B and LLaMA-2-70B workloads in the default run")
-    p.add_argument("--cpu-one-core", action="store_true",
-                   help="also time the CPU oracle on one thread (one whole pass; slow)")
+    p.add_argument("--cpu-one-core-sample", type=int, default=256, metavar="TOKENS",
+                   help="tokens of the one-thread pass of the CPU oracle (0: skip it)")
     return p.parse_args()
 
 
@@ -328,7 +329,22 @@ def cpu_baseline(path, n_sample: int, min_s: float = 10.0, threads: int = 0):
     return {"value": passes * n_sample / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"first {n_sample} tokens of the same workload, whole layer linear path "
                       f"(2 corrections + norms + quantisation + 4 GEMMs with the oracle's packed-code unpacking), "
-                      f"float64 numpy; {passes} pass(es) in {dt:.1f} s wall"}
+                      f"float64 numpy; {passes} pass(es) in {dt:.1f} s wall",
+            "host": host_cpu()}
+
+
+def host_cpu() -> dict:
+    """The host's processor model and logical CPU count (as the process sees them)."""
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"model": model, "logical_cpus": os.cpu_count()}
 
 
 def decode_leg(sites, ns=(1, 8, 64), copies: int = 12, iters: int = 200):
@@ -579,6 +595,22 @@ def main():
     def pct(q):
         return round(step_ms[min(len(step_ms) - 1, int(q * (len(step_ms) - 1) + 0.5))], 5)
 
+    # 4. the step's GEMM launches alone, back to back with events only around the
+    #    run (as in 1.): the roofline's per-launch time, free of the event gaps of
+    #    the per-stage pass
+    gemm_lists = [[fn for nm, kind, fn in sl if kind == "gemm"] for sl in stage_lists]
+    for i in range(args.warmup):
+        for fn in gemm_lists[i % len(copies)]:
+            fn()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(args.steps):
+        for fn in gemm_lists[i % len(copies)]:
+            fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    gemm_pass_ms = e0.elapsed_time(e1) / args.steps
+
     progress("timed region done; correction-off pass")
     # correction off: each site only normalises and quantises (one global rotation, T = I)
     off_lists = [p.stages(correction=False) for p in copies]
@@ -610,13 +642,31 @@ def main():
         torch.cuda.synchronize()
         ms_chain = e0.elapsed_time(e1) / args.steps
 
+    # 5. each stage alone and cold: one graph launches it once on each of ALONE_COPIES
+    #    buffer copies in turn (so its inputs come back only after more than twice the
+    #    Infinity Cache of other copies' traffic), replayed; no events between launches
+    alone_ms = {}
+    decode_sized = n <= 64
+    if not decode_sized:
+        progress(f"each stage alone over {ALONE_COPIES} buffer copies (cold, replayed graphs)")
+        extra = [base.clone() for _ in range(max(0, ALONE_COPIES - len(copies)))]
+        alone_lists = [p.stages() for p in copies + extra]
+        for j, nm in enumerate(names):
+            g = capture([sl[j][2] for sl in alone_lists])
+            alone_ms[nm] = replay_ms([g], 8, stream) / len(alone_lists)
+            del g
+        del extra, alone_lists
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+
     stages_out = {}
     gemm_ops = gemm_ms = gemm_launches = 0
     gemm_peak = FP4_PEAK_TOPS if base.fp4 else INT8_PEAK_TOPS
     for nm in names:
         byts, ops = base.stage_work(nm)
-        t = sum(stage_ms[nm]) / args.steps
-        rec = {"kind": kinds[nm], "ms": round(t, 5), "alg_bytes": byts}
+        t_ev = sum(stage_ms[nm]) / args.steps
+        t = alone_ms.get(nm, t_ev)
+        rec = {"kind": kinds[nm], "ms": round(t, 5), "ms_in_step_with_events": round(t_ev, 5), "alg_bytes": byts}
         rec["hbm_frac"] = round(byts / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
         if ops:
             rec["alg_ops"] = ops
@@ -641,7 +691,6 @@ def main():
     src_hash = kernel_source_hash()
     traffic = measured_traffic(cfg.name, src_hash)
     value = n / (ms_per_step * 1e-3)
-    decode_sized = n <= 64
     if decode_sized:
         # a few tokens: the GEMMs stream their weights once, so HBM bounds them. An eager
         # step of this size is bound by the host's launch rate, so the GEMM times come
@@ -658,10 +707,12 @@ def main():
                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                     "avg_launch_ms": round(gemm_ms / max(gemm_launches, 1), 5)}
     else:
+        gemm_ms = gemm_pass_ms
         achieved = gemm_ops / (gemm_ms * 1e-3) / 1e12
         roofline = {
             "kernel": ("qgemm_kernel (3-bit codes as fp4 on v_mfma_scale_f32_32x32x64_f8f6f4)" if base.fp4 else
-                       f"qgemm_kernel (int{cfg.bits} codes on v_mfma_i32_32x32x32_i8)") + ", all 4 launches of a step",
+                       f"qgemm_kernel (int{cfg.bits} codes on v_mfma_i32_32x32x32_i8)") +
+                      ", all 4 launches of a step, timed back to back without the other stages",
             "bound": "mfma",
             "achieved": round(achieved, 2),
             "peak": gemm_peak,
@@ -738,9 +789,11 @@ def main():
     if not args.no_cpu_baseline:
         progress(f"CPU oracle on a {min(args.cpu_sample, n)}-token sample")
         out["cpu_baseline"] = cpu_baseline(base, min(args.cpu_sample, n))
-        if args.cpu_one_core:
-            progress("CPU oracle on one thread")
-            out["cpu_baseline_one_core"] = cpu_baseline(base, min(args.cpu_sample, n), min_s=0.0, threads=1)
+        if args.cpu_one_core_sample > 0:
+            n1 = min(args.cpu_one_core_sample, n)
+            progress(f"CPU oracle on one thread, {n1}-token sample")
+            one = cpu_baseline(base, n1, min_s=0.0, threads=1)
+            out["cpu_baseline"]["one_core"] = {k: one[k] for k in ("value", "unit", "cores", "sample")}
     print(json.dumps(out), flush=True)
 
 
