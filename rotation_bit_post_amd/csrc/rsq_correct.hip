@@ -535,6 +535,7 @@ hipError_t launch_t(const void *h_in, void *h_out, int64_t n, int d, int64_t ld_
     // normalises and quantises the stored rows with the standalone quantiser
     if constexpr (CPW >= 4) {
         if (plan.cols) {
+            if (!grid_fits(blocks * CPW, 64 * nw)) return hipErrorInvalidConfiguration;
             hipLaunchKernelGGL((correct_kernel<T, CPW, R32, false, true>), dim3(static_cast<unsigned>(blocks * CPW)),
                                dim3(64 * nw), 0, s, hi, ho, n, d, ld_h, st, tb, nullptr, 0.0f, nullptr, nullptr);
             hipError_t e = hipGetLastError();
@@ -542,6 +543,7 @@ hipError_t launch_t(const void *h_in, void *h_out, int64_t n, int d, int64_t ld_
             return launch_quant(h_out, sizeof(T) == 2 ? 1 : 0, n, d, ld_h, true, norm_w, eps, bits, codes, scales, s);
         }
     }
+    if (!grid_fits(blocks, 64 * nw)) return hipErrorInvalidConfiguration;
     const dim3 grid(static_cast<unsigned>(blocks)), block(64 * nw);
     if constexpr (!QUANT) {
         hipLaunchKernelGGL((correct_kernel<T, CPW, R32, false>), grid, block, 0, s, hi, ho, n, d, ld_h, st, tb, norm_w,

@@ -568,6 +568,7 @@ template <int BITS, int TB, int NW, typename YT, int D = 2>
 hipError_t launch_gemv16(const uint8_t *a, const float *sa, int64_t n, const uint8_t *w, const float *sw, int64_t N,
                          int64_t K, void *y, int64_t ld_y, int32_t *acc_out, const void *res, int64_t ld_r,
                          hipStream_t s) {
+    if (!grid_fits(N / 16, NW * 64)) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((qgemv16_kernel<BITS, TB, NW, YT, D>), dim3(static_cast<unsigned>(N / 16)), dim3(NW * 64), 0,
                        s, a, sa, static_cast<int>(n), w, sw, static_cast<int>(N), static_cast<int>(K),
                        static_cast<YT *>(y), ld_y, acc_out, static_cast<const YT *>(res), ld_r);
@@ -578,6 +579,7 @@ template <int BITS, int TM, typename YT, int NW = 8>
 hipError_t launch_gemv(const uint8_t *a, const float *sa, int64_t n, const uint8_t *w, const float *sw, int64_t N,
                        int64_t K, void *y, int64_t ld_y, int32_t *acc_out, const void *res, int64_t ld_r,
                        hipStream_t s) {
+    if (!grid_fits((N + 31) / 32, NW * 64)) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((qgemv_kernel<BITS, TM, NW, YT>), dim3(static_cast<unsigned>((N + 31) / 32)), dim3(NW * 64), 0,
                        s, a, sa, static_cast<int>(n), w, sw, static_cast<int>(N), static_cast<int>(K),
                        static_cast<YT *>(y), ld_y, acc_out, static_cast<const YT *>(res), ld_r);
@@ -708,6 +710,7 @@ template <int BITS, int BM, int BN, int WM, int WN, typename YT, int P = 2>
 hipError_t launch_t(const uint8_t *a, const float *sa, int64_t n, const uint8_t *w, const float *sw, int64_t N,
                     int64_t K, void *y, int64_t ld_y, int32_t *acc_out, const void *res, int64_t ld_r, hipStream_t s) {
     const int64_t mt = (n + BM - 1) / BM, nt = (N + BN - 1) / BN;
+    if (!grid_fits(mt * nt, WM * WN * 64)) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((qgemm_kernel<BITS, BM, BN, WM, WN, P, YT>), dim3(static_cast<unsigned>(mt * nt)),
                        dim3(WM * WN * 64), 0, s, a, sa, static_cast<int>(n), w, sw, static_cast<int>(N),
                        static_cast<int>(K), static_cast<YT *>(y), ld_y, acc_out, static_cast<const YT *>(res), ld_r);

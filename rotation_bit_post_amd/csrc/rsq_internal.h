@@ -38,6 +38,13 @@ inline bool correct_geometry(int64_t d, bool f32, int *waves, int *chunks_per_wa
     return false;
 }
 
+// Whether `blocks` workgroups of `threads` threads fit one dispatch: fewer
+// than 2^31 workgroups and fewer than 2^32 threads in all. Launchers return
+// hipErrorInvalidConfiguration otherwise, rather than let a grid size wrap.
+inline bool grid_fits(int64_t blocks, int64_t threads) {
+    return blocks > 0 && blocks < (int64_t{1} << 31) && blocks * threads < (int64_t{1} << 32);
+}
+
 // Compute units of the current device (cached per device).
 int device_cus();
 

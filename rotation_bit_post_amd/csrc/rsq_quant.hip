@@ -153,6 +153,7 @@ template <typename T, int CH, int WPR>
 hipError_t launch_t(const void *x, int64_t n, int k, int64_t ld_x, bool norm, const float *norm_w, float eps,
                     int bits, uint8_t *codes, float *scales, hipStream_t s) {
     constexpr int RPB = 4 / WPR;
+    if (!grid_fits((n + RPB - 1) / RPB, kThreads)) return hipErrorInvalidConfiguration;
     const dim3 grid(static_cast<unsigned>((n + RPB - 1) / RPB));
     const T *xt = static_cast<const T *>(x);
     if (bits == 4)

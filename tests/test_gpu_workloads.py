@@ -244,7 +244,8 @@ def test_dense_comparator_against_oracle():
 
 
 @pytest.mark.parametrize("fp4", [False, True])
-@pytest.mark.parametrize("name,N,K", [("qkv_gqa", 6144, 4096), ("gate_up", 28672, 4096), ("down", 4096, 14336)])
+@pytest.mark.parametrize("name,N,K", [("qkv_gqa", 6144, 4096), ("qkv_mha", 12288, 4096), ("o", 4096, 4096),
+                                      ("gate_up", 28672, 4096), ("down", 4096, 14336)])
 def test_llama3_8b_w3a3_gemms_full_size(name, N, K, fp4):
     print(f"case llama3-8b w3a3 gemm {name} fp4={fp4}", flush=True)
     gemm_sampled(3, 4096, N, K, seed=N + K + 4, fp4=fp4)
@@ -298,7 +299,8 @@ def test_llama2_70b_site_full_batch():
     check_site(h, U, M, "bf16", cfg.bits, out, codes, scales)
 
 
-@pytest.mark.parametrize("name,N,K", [("qkv_gqa", 10240, 8192), ("gate_up", 57344, 8192), ("down", 8192, 28672)])
+@pytest.mark.parametrize("name,N,K", [("qkv_gqa", 10240, 8192), ("qkv_mha", 24576, 8192), ("o", 8192, 8192),
+                                      ("gate_up", 57344, 8192), ("down", 8192, 28672)])
 def test_llama2_70b_gemms_full_size(name, N, K):
     print(f"case llama2-70b gemm {name}", flush=True)
     gemm_sampled(4, 4096, N, K, seed=N + K + 5)
