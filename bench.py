@@ -120,25 +120,19 @@ def replay_ms(graphs, iters: int, stream) -> float:
 
 def copy_ceiling(nbytes: int, iters: int = 50):
     """Time of a plain device copy that moves nbytes (half read, half written), cold: the
-    copies rotate over more than twice the 256 MB Infinity Cache. The practical ceiling of a
-    stage that streams the same bytes once."""
+    copies rotate over more than twice the 256 MB Infinity Cache, launched as one replayed
+    HIP graph (as the stages are timed alone). The practical ceiling of a stage that
+    streams the same bytes once."""
     import torch
     half = max(nbytes // 2 // 16 * 16, 16)
     nbuf = max(2, int((600 << 20) // (2 * half)) + 1)
     src = [torch.ones(half, dtype=torch.uint8, device="cuda") for _ in range(nbuf)]
     dst = [torch.empty(half, dtype=torch.uint8, device="cuda") for _ in range(nbuf)]
     stream = torch.cuda.current_stream()
-    for i in range(nbuf):
-        dst[i].copy_(src[i])
+    g = capture([lambda i=i: dst[i].copy_(src[i]) for i in range(nbuf)])
+    ms = replay_ms([g], max(3, iters // nbuf), stream) / nbuf
+    del g, src, dst
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for i in range(iters):
-        dst[i % nbuf].copy_(src[i % nbuf])
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / iters
-    del src, dst
     torch.cuda.empty_cache()
     return ms
 
@@ -642,12 +636,28 @@ def main():
         torch.cuda.synchronize()
         ms_chain = e0.elapsed_time(e1) / args.steps
 
+    # when the step's value comes from replayed graphs, time the correction-off and the
+    # chained steps the same way, so that the overhead compares like with like
+    off_graph = chain_graph = None
+    if ms_graph is not None and ms_graph < ms_eager:
+        off_graph = replay_ms([p.capture(correction=False) for p in copies], args.steps, stream)
+        if ms_chain is not None:
+            chain_graph = replay_ms([p.capture(correction=True, chain=True) for p in copies], args.steps, stream)
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+
     # 5. each stage alone and cold: one graph launches it once on each of ALONE_COPIES
     #    buffer copies in turn (so its inputs come back only after more than twice the
     #    Infinity Cache of other copies' traffic), replayed; no events between launches
     alone_ms = {}
     decode_sized = n <= 64
-    if not decode_sized:
+    if decode_sized:
+        # a few tokens: an eager step is bound by the host's launch rate, so each stage
+        # is timed cold and alone in replayed graphs (decode_leg)
+        sites = {w: (st.U.cpu().numpy(), st.M.cpu().numpy()) for w, st in base.sites.items()}
+        leg = decode_leg(sites, ns=(n,))
+        alone_ms = {nm: leg[str(n)]["stages"][nm]["ms"] for nm in names}
+    else:
         progress(f"each stage alone over {ALONE_COPIES} buffer copies (cold, replayed graphs)")
         extra = [base.clone() for _ in range(max(0, ALONE_COPIES - len(copies)))]
         alone_lists = [p.stages() for p in copies + extra]
@@ -692,11 +702,8 @@ def main():
     traffic = measured_traffic(cfg.name, src_hash)
     value = n / (ms_per_step * 1e-3)
     if decode_sized:
-        # a few tokens: the GEMMs stream their weights once, so HBM bounds them. An eager
-        # step of this size is bound by the host's launch rate, so the GEMM times come
-        # from replayed graphs, each stage cold (decode_leg)
-        sites = {w: (st.U.cpu().numpy(), st.M.cpu().numpy()) for w, st in base.sites.items()}
-        leg = decode_leg(sites, ns=(n,))
+        # a few tokens: the GEMMs stream their weights once, so HBM bounds them; their
+        # times are the cold replayed-graph times of decode_leg
         gemm_nm = [nm for nm in names if kinds[nm] == "gemm"]
         gemm_bytes = sum(leg[str(n)]["stages"][nm]["alg_bytes"] for nm in gemm_nm)
         gemm_ms = sum(leg[str(n)]["stages"][nm]["ms"] for nm in gemm_nm)
@@ -746,17 +753,18 @@ def main():
         "roofline": roofline,
         "stages": stages_out,
         "correction_overhead": {
-            "ms_per_step_correction_off": round(ms_off, 5),
-            "overhead_frac": round(ms_eager / ms_off - 1.0, 4),
+            "ms_per_step_correction_off": round(off_graph if off_graph is not None else ms_off, 5),
+            "overhead_frac": round((ms_per_step / off_graph if off_graph is not None else ms_eager / ms_off) - 1.0, 4),
             "note": "same path with each site reduced to RMSNorm + quantisation (T = I, a single global rotation); "
-                    "both launched eagerly",
+                    + ("both replayed as HIP graphs" if off_graph is not None else "both launched eagerly"),
         },
         "layer_chained": None if ms_chain is None else {
-            "ms_per_step": round(ms_chain, 5),
-            "tokens_per_s": round(n / (ms_chain * 1e-3), 1),
+            "ms_per_step": round(chain_graph if chain_graph is not None else ms_chain, 5),
+            "tokens_per_s": round(n / ((chain_graph if chain_graph is not None else ms_chain) * 1e-3), 1),
             "note": "the same stages with the residual stream carried through: o_proj and down_proj "
                     "outputs added to the corrected residual inside the GEMM epilogue (rsq_qgemm_residual), "
-                    "site B reading h2; timed back to back, no events between stages",
+                    "site B reading h2; " + ("replayed as HIP graphs" if chain_graph is not None else
+                                             "timed back to back, no events between stages"),
         },
         "timing": {
             "ms_per_step_eager": round(ms_eager, 5),
