@@ -49,7 +49,11 @@
  *    accumulator bound), k <= 32768 for rsq_quant_act (one row in the
  *    registers of at most four waves); for the correction d / 32 must split
  *    into at most 8 waves of 1, 2, 4, 8, 16 or 32 column chunks (at most 16
- *    for a float32 residual), i.e. d <= 8192 (4096 for float32).
+ *    for a float32 residual), i.e. d <= 8192 (4096 for float32). A launch that
+ *    would need more than 2^31 workgroups or 2^32 threads in one dispatch
+ *    is refused with RSQ_ERR_HIP instead of being enqueued (buffers of such
+ *    sizes exceed a device's memory; rsq_layer_fused may then already have
+ *    enqueued its correction).
  */
 #ifndef RSQ_H
 #define RSQ_H
