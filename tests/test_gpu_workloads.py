@@ -95,7 +95,7 @@ def gemm_sampled(bits, n, N, K, seed, rows=None, cols=None, y_dtype="bf16", fp4=
         rsq.rsq_qgemm(torch.from_numpy(a_bytes).cuda(), to_dev(sa, "f32"), n, torch.from_numpy(w_bytes).cuda(),
                       to_dev(sw, "f32"), N, K, bits, y, acc_out=acc)
     torch.cuda.synchronize()
-    rows = rows if rows is not None else np.unique(np.r_[0, rng.choice(n, min(n, 96), replace=False), n - 1])
+    rows = rows if rows is not None else np.unique(np.r_[0, rng.choice(n, min(n, 256), replace=False), n - 1])
     cols = cols if cols is not None else np.unique(np.r_[0, rng.choice(N, min(N, 384), replace=False), N - 1])
     qa = packing.unpack(a_bytes[rows], K, bits)
     qw = packing.unpack(w_bytes[cols], K, bits)
