@@ -57,6 +57,7 @@ CORRECT_CASES = [  # dtype, d, r, n
     ("bf16", 1024, 32, 33), ("bf16", 512, 64, 40), ("f32", 128, 16, 5), ("bf16", 2048, 2, 1),
     ("f32", 1024, 40, 19),
     ("f32", 4096, 32, 20),   # the widest float32 residual
+    ("bf16", 8192, 64, 9),   # the widest residual at the largest rank (column-split form)
 ]
 
 
@@ -167,7 +168,10 @@ def test_quant_act_matches_oracle(dtype, n, k, bits, norm, weighted):
 def test_fused_correct_quant_equals_unfused_and_oracle():
     rsq = lib()
     import torch
-    for dtype, d, r, n, bits in [("bf16", 1024, 32, 45, 4), ("bf16", 512, 16, 8, 3), ("f32", 256, 8, 16, 4)]:
+    # the last two: the widest residual at the largest rank (32 chunks per wave, two rank blocks) on
+    # the full-block path, and the widest float32 residual at the largest rank
+    for dtype, d, r, n, bits in [("bf16", 1024, 32, 45, 4), ("bf16", 512, 16, 8, 3), ("f32", 256, 8, 16, 4),
+                                 ("bf16", 8192, 64, 300, 4), ("f32", 4096, 64, 200, 3)]:
         print(f"case fused dtype={dtype} d={d} r={r} n={n} bits={bits}", flush=True)
         U, M = random_site(d, r, seed=11)
         site = gpu_site(U, M)
