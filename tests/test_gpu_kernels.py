@@ -488,12 +488,15 @@ def test_qgemm_strided_output_and_minimum_codes():
     assert torch.all(y[:, :N] == float(64 * K)) and torch.all(y[:, N:] == -1.0)
 
 
-@pytest.mark.parametrize("dtype,d,r,n,N,bits", [("f32", 256, 8, 16, 256, 4), ("bf16", 4096, 32, 300, 4096, 3)])
-def test_layer_fused_matches_oracle(dtype, d, r, n, N, bits):
+@pytest.mark.parametrize("dtype,d,r,n,N,bits,in_place", [
+    ("f32", 256, 8, 16, 256, 4, False), ("bf16", 4096, 32, 300, 4096, 3, False),
+    # decode sizes: the column-split site and the 16-channel GEMM; in place, the full-block site
+    ("bf16", 4096, 32, 1, 12288, 4, False), ("bf16", 4096, 32, 8, 4096, 3, False), ("bf16", 4096, 32, 8, 4096, 4, True)])
+def test_layer_fused_matches_oracle(dtype, d, r, n, N, bits, in_place):
     """One site and its linear in one call (the second case takes the prefill tiles and int3 codes)."""
     rsq = lib()
     import torch
-    print(f"case layer_fused dtype={dtype} d={d} r={r} n={n} N={N} bits={bits}", flush=True)
+    print(f"case layer_fused dtype={dtype} d={d} r={r} n={n} N={N} bits={bits} in_place={in_place}", flush=True)
     U, M = random_site(d, r, seed=21) if d <= 1024 else subspace_site(d, r, seed=21)
     site = gpu_site(U, M)
     h = residual(n, d, dtype, seed=22)
@@ -502,7 +505,7 @@ def test_layer_fused_matches_oracle(dtype, d, r, n, N, bits):
     wp = packing.pack(qw, bits)
     hd = to_dev(h, dtype)
     rb = rsq.rsq_packed_row_bytes(d, bits)
-    h_out, codes, scales = torch.empty_like(hd), empty_u8(n, rb), empty_f32(n)
+    h_out, codes, scales = (hd if in_place else torch.empty_like(hd)), empty_u8(n, rb), empty_f32(n)
     y = torch.empty((n, N), dtype=torch.float32 if dtype == "f32" else torch.bfloat16, device="cuda")
     rsq.rsq_layer_fused(hd, h_out, site, r, codes, scales, torch.from_numpy(wp).cuda(), to_dev(sw, "f32"), N, y, bits)
     torch.cuda.synchronize()
