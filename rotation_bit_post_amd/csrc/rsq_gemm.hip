@@ -745,23 +745,23 @@ hipError_t launch_b(const uint8_t *a, const float *sa, int64_t n, const uint8_t 
         // workgroup re-reads all 64 activation rows)
         // long k: more k steps in flight (up to 16 tokens: 4 waves with a
         // 3-step ring, e.g. 1 token at K = 11008: 6.5 against 7.5 us for 8
-        // waves with 2; more tokens: 8 waves with 2)
-        // up to 16 tokens on a layer wide enough for more than four rounds of
-        // 16-channel workgroups: 32-channel workgroups of 4 waves instead
-        // (gate|up, 22016 x 4096: 8 tokens 13.5 against 14.6 us, 16 tokens 15.1
-        // against 16.8 us; equal at 1 token)
-        if (n <= 16 && N / 16 > 4 * cus && K < 8192)
-            return launch_gemv<BITS, 1, YT, 4>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s);
+        // waves with 2; more tokens: 8 waves with 2). A layer whose 16-channel
+        // workgroups fit the CUs in one round takes 8 waves as well (o, 4096 x
+        // 4096: 1 token 4.7 against 5.4 us, 8 tokens 5.0 against 5.7, 64
+        // tokens 9.2 against 9.9; the widest layers keep 4: gate|up, 22016 x
+        // 4096, 8 tokens 14.7 against 16.2 us).
         if (n <= 16 || (n <= 64 && N / 16 <= cus)) {
             const bool deep = K >= 8192;
+            const bool wide = deep || N / 16 <= cus;   // 8 waves per workgroup
             switch ((n + 15) / 16) {
             case 1: return deep ? launch_gemv16<BITS, 1, 4, YT, 3>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s)
-                                : launch_gemv16<BITS, 1, 4, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s);
-            case 2: return deep ? launch_gemv16<BITS, 2, 8, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s)
+                                : (wide ? launch_gemv16<BITS, 1, 8, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s)
+                                        : launch_gemv16<BITS, 1, 4, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s));
+            case 2: return wide ? launch_gemv16<BITS, 2, 8, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s)
                                 : launch_gemv16<BITS, 2, 4, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s);
-            case 3: return deep ? launch_gemv16<BITS, 3, 8, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s)
+            case 3: return wide ? launch_gemv16<BITS, 3, 8, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s)
                                 : launch_gemv16<BITS, 3, 4, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s);
-            default: return deep ? launch_gemv16<BITS, 4, 8, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s)
+            default: return wide ? launch_gemv16<BITS, 4, 8, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s)
                                  : launch_gemv16<BITS, 4, 4, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s);
             }
         }
