@@ -765,14 +765,21 @@ hipError_t launch_b(const uint8_t *a, const float *sa, int64_t n, const uint8_t 
                                  : launch_gemv16<BITS, 4, 4, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s);
             }
         }
+        // 17-64 tokens on the wider layers: 32-channel workgroups while they fit
+        // the CUs in one round (up to 48 tokens), else 32 x 32 tiles up to 32
+        // tokens and 64 x 64 tiles beyond (64 x 64 tiles halve the re-reads of
+        // the activation rows of 64 x 32 tiles: q|k|v at 64 tokens 13.1 against
+        // 15.2 us). Measured as graph replays: 32-channel workgroups in two
+        // rounds are the slowest choice (q|k|v, 12288 x 4096, 32 tokens: 14.7
+        // against 11.4 us on 32 x 32 tiles); in one round the fastest up to 48
+        // tokens (6144 x 4096, 24 tokens: 8.0 against 12.2 us).
         if (n <= 32) {
-            if (gemv_wgs <= 2 * cus) return launch_gemv<BITS, 1, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s);
+            if (gemv_wgs <= cus) return launch_gemv<BITS, 1, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s);
             return launch_t<PK, 32, 32, 1, 1, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s);
         }
         if (n <= 64) {
-            // 64 x 64 tiles: half the re-reads of the activation rows of 64 x 32
-            // tiles (q|k|v at 64 tokens: 13.1 against 15.2 us; gate|up equal)
-            if (gemv_wgs <= cus) return launch_gemv<BITS, 2, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s);
+            if (gemv_wgs <= cus && n <= 48)
+                return launch_gemv<BITS, 2, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s);
             return launch_t<PK, 64, 64, 2, 2, YT>(a, sa, n, w, sw, N, K, y, ld_y, acc_out, res, ld_r, s);
         }
     }

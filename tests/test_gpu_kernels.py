@@ -214,6 +214,8 @@ GEMM_CASES = [  # bits, n, N, K, y dtype
     # int4 packed in LDS on the decode-size tiles: 64 x 64 (50 tokens) and 32 x 32 (27 tokens),
     # ragged channels and a partial 256-code k step
     (4, 50, 8224, 4128, "bf16"), (4, 27, 16448, 1056, "f32"),
+    # 32-channel decode kernel in one round of workgroups: one and two 32-token fragments
+    (4, 24, 6144, 4096, "bf16"), (3, 40, 8192, 1056, "f32"),
 ]
 
 
